@@ -1,0 +1,326 @@
+"""Pins of the fp64 CPU oracle against things other than itself (CPU only).
+
+Each pin is chosen so that a plausible slip in the oracle (a dropped term, a
+wrong sign or index, a transposed operand, a wrong tie rule or rounding) fails
+at least one test here.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import softmax
+
+import oracle
+from mixture_experts_layer_13_amd import inputs
+from tests import bruteforce as bf
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- codecs
+
+def test_e4m3_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(256):
+        v = oracle.e4m3_to_f64(c)
+        if math.isnan(ref[c]):
+            assert math.isnan(v), c
+        else:
+            assert v == ref[c] and math.copysign(1, v) == math.copysign(1, ref[c]), c
+    assert oracle.e4m3_to_f64(0x7E) == 448.0
+    assert oracle.e4m3_to_f64(0x01) == 2.0 ** -9
+
+
+def _e4m3_grid():
+    pos = np.array(sorted({oracle.e4m3_to_f64(c) for c in range(0x7F)}), np.float64)
+    mids = (pos[1:] + pos[:-1]) / 2  # exact ties
+    pts = [pos, mids]
+    f32 = mids.astype(np.float32)
+    pts += [np.nextafter(f32, np.float32(np.inf)).astype(np.float64),
+            np.nextafter(f32, np.float32(-np.inf)).astype(np.float64)]
+    rng = np.random.default_rng(7)
+    pts.append(rng.uniform(0, 520, 4000))
+    pts.append(np.exp(rng.uniform(-14, 6.3, 4000)))
+    pts.append(np.array([448.0, 449.0, 463.9, 464.0, 500.0, 1e30, 2.0 ** -10, 2.0 ** -11]))
+    v = np.concatenate(pts).astype(np.float32)
+    return np.concatenate([v, -v])
+
+
+def test_e4m3_encode_matches_clamped_torch_cast():
+    v = _e4m3_grid()
+    ref = torch.from_numpy(v).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_from_f32(float(a)) for a in v], np.uint8)
+    # -0.0 and +0.0 carry their sign in both
+    assert np.array_equal(got, ref), v[got != ref][:10]
+
+
+def test_e4m3_ties_to_even_and_saturation():
+    assert oracle.e4m3_from_f32(1.0625) == 0x38      # between 1.0 (0x38) and 1.125 (0x39)
+    assert oracle.e4m3_from_f32(1.1875) == 0x3A      # between 1.125 and 1.25 -> even 0x3A
+    assert oracle.e4m3_from_f32(2.0 ** -10) == 0x00  # half of the smallest subnormal
+    assert oracle.e4m3_from_f32(1e9) == 0x7E
+    assert oracle.e4m3_from_f32(-1e9) == 0xFE
+    assert oracle.e4m3_from_f32(float("inf")) == 0x7E
+
+
+def test_bf16_decode_matches_torch():
+    rng = np.random.default_rng(3)
+    bits = rng.integers(0, 65536, 5000).astype(np.uint16)
+    ref = bf.decode(bits)
+    for b, r in zip(bits, ref):
+        v = oracle.bf16_to_f64(int(b))
+        assert (math.isnan(v) and math.isnan(r)) or v == r
+
+
+def test_act_scale_and_amax_element_maps_to_448():
+    rng = np.random.default_rng(11)
+    for trial in range(20):
+        x = (rng.standard_normal(777) * 10 ** rng.uniform(-3, 3)).astype(np.float32)
+        s = oracle.act_scale(x)
+        assert s == np.float32(np.float32(np.abs(x).max()) / np.float32(448))
+        q = oracle.quantize_e4m3(x, s)
+        i = int(np.abs(x).argmax())
+        assert q[i] in (0x7E, 0xFE)
+        # codes equal torch's cast of the fp32 quotient
+        ref = torch.from_numpy(x / s).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(q, ref)
+    assert oracle.act_scale(np.zeros(8, np.float32)) == 1.0
+
+
+# ---------------------------------------------------------------- routing
+
+@pytest.mark.parametrize("T,E,k", [(16, 8, 2), (64, 64, 8), (5, 256, 8), (3, 1024, 64), (7, 2, 1)])
+def test_route_matches_full_sort(T, E, k):
+    rng = np.random.default_rng(T * 1000 + E)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[0, : min(E, 4)] = 0.5  # ties inside the top-k
+    for renorm in (True, False):
+        ids, w = oracle.route_topk(logits, k, renorm)
+        rids, rw = bf.route(logits, k, renorm)
+        assert np.array_equal(ids, rids)
+        np.testing.assert_allclose(w, rw, rtol=1e-13, atol=0)
+
+
+def test_route_all_equal_logits_tie_break_to_lower_id():
+    logits = np.zeros((3, 16), np.float32)
+    logits[1] = -0.0
+    logits[2, ::2] = -0.0  # -0 and +0 compare equal
+    ids, w = oracle.route_topk(logits, 5, True)
+    assert np.array_equal(ids, np.tile(np.arange(5, dtype=np.int32), (3, 1)))
+    assert np.allclose(w, 0.2, rtol=0, atol=1e-15)
+
+
+def test_route_k_equals_e_is_full_softmax():
+    rng = np.random.default_rng(5)
+    logits = (rng.standard_normal((9, 32)) * 3).astype(np.float32)
+    ids, w = oracle.route_topk(logits, 32, True)
+    p = softmax(logits.astype(np.float64), axis=1)
+    np.testing.assert_allclose(w, np.take_along_axis(p, ids.astype(np.int64), 1), rtol=1e-13)
+    # slots are in non-increasing probability order
+    assert np.all(np.diff(w, axis=1) <= 0)
+
+
+def test_route_two_experts_top1_is_sigmoid_or_one():
+    l = np.array([[0.3, -1.2], [2.0, 2.5]], np.float32)
+    ids, w = oracle.route_topk(l, 1, True)
+    assert np.array_equal(ids[:, 0], [0, 1]) and np.all(w == 1.0)
+    ids, w = oracle.route_topk(l, 1, False)
+    d = np.float64(l[:, 0]) - np.float64(l[:, 1])
+    sig = 1 / (1 + np.exp(-np.abs(d)))
+    np.testing.assert_allclose(w[:, 0], sig, rtol=1e-14)
+
+
+def test_route_weight_invariants():
+    rng = np.random.default_rng(9)
+    logits = rng.standard_normal((50, 64)).astype(np.float32)
+    _, w = oracle.route_topk(logits, 8, True)
+    np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-14)
+    assert np.all(w >= 0) and np.all(np.diff(w, axis=1) <= 0)
+
+
+def test_route_golden_closed_form():
+    g = json.load(open(os.path.join(GOLDEN, "closed_forms.json")))["route"]
+    l = np.log(np.array([g["logits_ln_of"]], np.float64)).astype(np.float32)
+    ids, w = oracle.route_topk(l, g["topk"], True)
+    assert list(ids[0]) == g["ids"]
+    np.testing.assert_allclose(w[0], g["weights_renorm"], rtol=1e-6)
+    _, w = oracle.route_topk(l, g["topk"], False)
+    np.testing.assert_allclose(w[0], g["weights_plain"], rtol=1e-6)
+
+
+# ------------------------------------------------------------------ align
+
+@pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("T,E,k", [(1, 64, 8), (16, 8, 2), (64, 64, 8), (37, 256, 8), (300, 8, 3)])
+def test_align_matches_sorted_bruteforce(bm, T, E, k):
+    rng = np.random.default_rng(T + E + bm)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    if E > 8:
+        logits += inputs.zipf_log_bias(E, 1.1).numpy().astype(np.float32)
+    ids, _ = oracle.route_topk(logits, k, True)
+    got = oracle.align(ids, E, bm)
+    ref = bf.align(ids, E, bm)
+    for key in ("sorted_pair_ids", "block_expert_ids", "expert_offsets", "pair_pos"):
+        assert np.array_equal(got[key], ref[key]), key
+    assert got["num_padded"] == ref["num_padded"]
+
+
+def test_align_invariants_and_capacity():
+    rng = np.random.default_rng(1)
+    for T, E, k, bm in [(64, 64, 8, 16), (256, 256, 8, 64), (1, 8, 2, 256), (2, 3, 3, 32)]:
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+        ids, _ = oracle.route_topk(logits, k, True)
+        a = oracle.align(ids, E, bm)
+        P = T * k
+        s = a["sorted_pair_ids"]
+        assert a["num_padded"] % bm == 0
+        assert a["num_padded"] <= oracle.align_capacity(T, k, E, bm)
+        assert sorted(s[s < P].tolist()) == list(range(P))
+        assert np.all(s[a["pair_pos"]] == np.arange(P))
+        off = a["expert_offsets"]
+        assert np.all(np.diff(off) % bm == 0) and off[-1] == a["num_padded"]
+        flat = ids.reshape(-1)
+        for e in range(E):
+            seg = s[off[e]:off[e + 1]]
+            real = seg[seg < P]
+            assert np.all(flat[real] == e) and np.all(np.diff(real) > 0)
+            assert np.all(seg[len(real):] == P)  # padding only at the tail
+            assert np.all(a["block_expert_ids"][off[e] // bm: off[e + 1] // bm] == e)
+
+
+def test_align_empty_batch():
+    a = oracle.align(np.zeros((0, 4), np.int32), 8, 16)
+    assert a["num_padded"] == 0 and np.all(a["expert_offsets"] == 0)
+
+
+# ---------------------------------------------------------------- forward
+
+def _tiny(T=6, H=32, I=16, E=5, k=2, seed=0, dtype="f32"):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((T, H)) * 0.5).astype(np.float32)
+    w13 = (rng.standard_normal((E, 2 * I, H)) * 0.2).astype(np.float32)
+    w2 = (rng.standard_normal((E, H, I)) * 0.2).astype(np.float32)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    if dtype == "bf16":
+        conv = lambda a: torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        x, w13, w2 = conv(x), conv(w13), conv(w2)
+    return x, w13, w2, logits
+
+
+def test_forward_single_expert_top1_is_dense_swiglu_mlp():
+    x, w13, w2, logits = _tiny(T=9, H=48, I=24, E=1, k=1, seed=2)
+    ids, w = oracle.route_topk(logits, 1, True)
+    out, _ = oracle.moe_forward(x, w13, w2, ids, w)
+    X, W13, W2 = (a.astype(np.float64) for a in (x, w13[0], w2[0]))
+    g = np.matmul(X, W13[:24].T)
+    u = np.matmul(X, W13[24:].T)
+    ref = np.matmul(g / (1 + np.exp(-g)) * u, W2.T)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("renorm", [True, False])
+def test_forward_matches_dense_gated_formula(dtype, renorm):
+    x, w13, w2, logits = _tiny(T=7, H=40, I=24, E=6, k=3, seed=4, dtype=dtype)
+    ids, w = oracle.route_topk(logits, 3, renorm)
+    out, s = oracle.moe_forward(x, w13, w2, ids, w)
+    assert s == (1.0, 1.0)
+    ref = bf.dense_gated(bf.decode(x), bf.decode(w13), bf.decode(w2), ids, w)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-14)
+
+
+def test_forward_zero_input_and_linear_in_w2():
+    x, w13, w2, logits = _tiny(seed=8)
+    ids, w = oracle.route_topk(logits, 2, True)
+    z, _ = oracle.moe_forward(np.zeros_like(x), w13, w2, ids, w)
+    assert np.all(z == 0)
+    o1, _ = oracle.moe_forward(x, w13, w2, ids, w)
+    o2, _ = oracle.moe_forward(x, w13, (w2 * 2).astype(np.float32), ids, w)
+    assert np.array_equal(o2, 2 * o1)
+
+
+def test_forward_token_permutation_equivariance():
+    x, w13, w2, logits = _tiny(T=11, seed=12)
+    perm = np.random.default_rng(0).permutation(11)
+    ids, w = oracle.route_topk(logits, 2, True)
+    o, _ = oracle.moe_forward(x, w13, w2, ids, w)
+    ids2, w2r = oracle.route_topk(logits[perm], 2, True)
+    o2, _ = oracle.moe_forward(x[perm], w13, w2, ids2, w2r)
+    assert np.array_equal(o2, o[perm])
+
+
+def test_forward_expert_relabelling_invariance():
+    x, w13, w2, logits = _tiny(T=8, E=7, seed=13)
+    perm = np.random.default_rng(1).permutation(7)  # new expert i is old perm[i]
+    ids, w = oracle.route_topk(logits, 2, True)
+    o, _ = oracle.moe_forward(x, w13, w2, ids, w)
+    ids2, wb = oracle.route_topk(np.ascontiguousarray(logits[:, perm]), 2, True)
+    o2, _ = oracle.moe_forward(x, np.ascontiguousarray(w13[perm]), np.ascontiguousarray(w2[perm]), ids2, wb)
+    assert np.array_equal(perm[ids2], ids)
+    assert np.array_equal(o2, o)
+
+
+def test_forward_token_subset_equals_full_rows():
+    x, w13, w2, logits = _tiny(T=10, seed=14)
+    ids, w = oracle.route_topk(logits, 2, True)
+    full, _ = oracle.moe_forward(x, w13, w2, ids, w)
+    sub, _ = oracle.moe_forward(x, w13, w2, ids, w, tokens=np.array([7, 2, 9]))
+    assert np.array_equal(sub, full[[7, 2, 9]])
+
+
+def test_forward_golden_closed_form_ffn():
+    g = json.load(open(os.path.join(GOLDEN, "closed_forms.json")))["ffn"]
+    x = np.array([[g["x"]]], np.float32)
+    w13 = np.array([[[math.log(g["gate_ln_of"])], [g["up"]]]], np.float32)
+    w2 = np.array([[[g["down"]]]], np.float32)
+    out, _ = oracle.moe_forward(x, w13, w2, np.zeros((1, 1), np.int32), np.ones((1, 1)))
+    assert abs(out[0, 0] / math.log(3.0) - g["out_times_inverse_ln3"]) < 1e-7
+
+
+def _fp8_case(T=9, H=64, I=32, E=6, k=3, seed=21):
+    w = inputs.WORKLOADS["decode_fp8"]
+    d = inputs.make_inputs(w, T, device="cpu", seed=seed, H=H, I=I, E=E, topk=k)
+    return {key: (inputs.to_numpy_bits(v) if isinstance(v, torch.Tensor) else v)
+            for key, v in d.items()}
+
+
+def test_forward_fp8_matches_torch_cast_bruteforce():
+    d = _fp8_case()
+    ids, w = oracle.route_topk(d["logits"], d["topk"], True)
+    out, (sx, sh) = oracle.moe_forward(d["x"], d["w13"], d["w2"], ids, w, d["w13_scale"],
+                                       d["w2_scale"], fp8_act=True)
+    ref, rsx, rsh = bf.fp8_forward(d["x"], d["w13"], d["w2"], d["w13_scale"], d["w2_scale"], ids, w)
+    assert sx == rsx and sh == rsh
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-13)
+
+
+def test_forward_fp8_weights_without_act_quant_match_dense_gated():
+    d = _fp8_case(seed=22)
+    ids, w = oracle.route_topk(d["logits"], d["topk"], True)
+    out, _ = oracle.moe_forward(d["x"], d["w13"], d["w2"], ids, w, d["w13_scale"], d["w2_scale"])
+    w13d = bf.decode(d["w13"]) * d["w13_scale"].astype(np.float64)[:, None, None]
+    w2d = bf.decode(d["w2"]) * d["w2_scale"].astype(np.float64)[:, None, None]
+    ref = bf.dense_gated(bf.decode(d["x"]), w13d, w2d, ids, w)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-13)
+
+
+def test_forward_fp8_static_scales_are_used():
+    d = _fp8_case(seed=23)
+    ids, w = oracle.route_topk(d["logits"], d["topk"], True)
+    _, (sx, sh) = oracle.moe_forward(d["x"], d["w13"], d["w2"], ids, w, d["w13_scale"],
+                                     d["w2_scale"], fp8_act=True, a1_scale=0.125, a2_scale=0.5)
+    assert (sx, sh) == (0.125, 0.5)
+
+
+def test_pages_dimensions_golden():
+    g = json.load(open(os.path.join(GOLDEN, "pages_dims.json")))
+    for name in ("decode_bf16", "decode_fp8", "prefill_bf16", "prefill_fp8"):
+        w = inputs.WORKLOADS[name]
+        assert w.topk == g["topk"]
+        assert w.topk * w.I == g["aggregate_N"]
+        assert w.H == g["dense_hidden"]
+    assert min(inputs.WORKLOADS["decode_bf16"].tokens) == g["decode_rows_min"]
