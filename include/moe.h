@@ -1,0 +1,224 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) fused Mixture-of-Experts layer.
+ *
+ * Pages cited (titles as published):
+ *   [post]    "Amazon SageMaker AI 上的 Mixture-of-Experts 内核工程优化"
+ *             (English text of the AWS Machine Learning Blog post).
+ *   [digest]  "AWS公布SageMaker AI上MoE融合内核的三项优化，H200吞吐提升最高 10%".
+ *   [faq]     uniquestudio AI-news digest of the same post.
+ *
+ * The layer is one batched device operation made of three calls, issued in
+ * this order on one stream: moe_route_topk -> moe_align_permute ->
+ * moe_fused_forward ([post], introduction: routing, shuffling and the expert
+ * networks merged into one batched op instead of a per-expert loop).
+ *
+ * Naming follows the expert GEMM statement A[M,K] x B[K,N] -> C[M,N] of
+ * [post], "Swap-AB for WGMMA utilization": M = token rows (T), K = hidden
+ * features (H), N = per-expert intermediate size (I; the gate/up projection
+ * emits 2N).  Weights are passed already transposed, B^T[N,K] with K
+ * contiguous ([faq], "背景与事实", the B^T[N,K] x A^T[K,M] form):
+ *   w13 [E][2N][K]  rows [0,N) gate, rows [N,2N) up;   w2 [E][K][N].
+ *
+ * Conventions shared by every call:
+ *   - Pointers named as device buffers are device pointers (hipMalloc or
+ *     torch CUDA tensors), row-major and densely packed; activations,
+ *     weights, outputs and workspaces 16-byte aligned, index, weight-of-
+ *     routing and scale buffers 4-byte aligned (MOE_ERR_ALIGN otherwise).  The
+ *     caller allocates and owns every buffer, including the workspace; the
+ *     library keeps no pointer after returning and never allocates, frees,
+ *     synchronises or reads device memory from the host.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).  All
+ *     work is enqueued on it asynchronously; the calls can be captured into a
+ *     HIP graph.  The token count M is only ever a kernel argument: no call
+ *     compiles, allocates or waits for a new M (the lesson of [post], "Triton
+ *     JIT recompilation elimination").
+ *   - Every argument is validated on the host before anything is launched; a
+ *     non-zero status means nothing was enqueued.  MOE_ERR_HIP means a launch
+ *     was rejected by the runtime.  Faults inside kernels surface at the
+ *     caller's next synchronisation.  moe_last_error() describes the last
+ *     failure of the calling thread.
+ *   - M == 0 is valid: after the size checks the call returns MOE_OK and
+ *     enqueues nothing (buffers may then be NULL), except where documented.
+ *   - Calls are reentrant; concurrent calls must not share output or
+ *     workspace buffers.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  MOE_ERR_DTYPE = 3,       /* an unknown dtype code */
+  MOE_ERR_ALIGN = 4,       /* a pointer is not aligned as required */
+  MOE_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+  MOE_ERR_UNSUPPORTED = 6, /* valid values this build does not handle */
+  MOE_ERR_HIP = 7          /* the HIP runtime rejected a launch */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* Problem description for moe_workspace_size / moe_fused_forward.
+ *   M        token rows T, >= 0.
+ *   K        hidden size H, multiple of 128, <= 65536.
+ *   N        expert intermediate size I, multiple of 128, <= 65536.
+ *   E        experts, 1..1024.
+ *   topk     experts per token, 1..min(E, 64).
+ *   block_m  segment padding used by moe_align_permute: 16, 32, 64, 128, 256.
+ *   a_dtype  activations x: MOE_F32 or MOE_BF16.
+ *   w_dtype  weights: MOE_F32, MOE_BF16 (computed on bf16 MFMA, fp32
+ *            accumulate; f32 values are rounded to bf16 on load) or
+ *            MOE_FP8_E4M3 (OCP E4M3FN codes with one fp32 scale per expert
+ *            and matrix; activations are then quantised to E4M3 per tensor,
+ *            [post], "Backend routing for FP8 tensor quantization").
+ *   out_dtype  MOE_F32 or MOE_BF16. */
+typedef struct {
+  int32_t M, K, N, E, topk, block_m;
+  int32_t a_dtype, w_dtype, out_dtype;
+} moe_problem;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_string(int32_t status);
+
+/* Description of the last failing call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Upper bound of the padded pair list: P + min(E, P) * (block_m - 1) with
+ * P = M * topk.  Returns -1 for invalid arguments.  Host only. */
+int64_t moe_align_capacity(int32_t M, int32_t topk, int32_t E, int32_t block_m);
+
+/* Bytes of device workspace that moe_align_permute and moe_fused_forward
+ * need for problem *p (one buffer serves both calls; its contents need no
+ * initialisation and are not preserved between calls).  Host only. */
+moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
+
+/*
+ * Top-k routing ([post], introduction, "token routing"; k experts per token,
+ * uniquestudio digest, "背景与事实").  For every token row t:
+ *   ids[t, 0:k]  the k expert ids with the largest logits, in descending
+ *                logit order; equal logits go to the lower expert id
+ *                (-0.0 and +0.0 are equal).  Selection compares the raw fp32
+ *                logits, so ids are exact.
+ *   w[t, j]      softmax probability of ids[t,j] in fp32; with
+ *                renormalize != 0 divided by the sum over the k selected.
+ * logits     device f32 [M, E]; finite values (NaN/Inf give unspecified ids).
+ * topk_ids   device int32 [M, topk]  (written).
+ * topk_weights device f32 [M, topk]  (written).
+ * Limits: 1 <= E <= 1024, 1 <= topk <= min(E, 64), M >= 0.
+ */
+moe_status moe_route_topk(const float* logits, int32_t M, int32_t E,
+                          int32_t topk, int32_t renormalize, int32_t* topk_ids,
+                          float* topk_weights, void* stream);
+
+/*
+ * Per-expert token bucketing ([post], "Backend routing for FP8 tensor
+ * quantization": small, fragmented token groups mapped onto the active
+ * experts' weights).  Stable counting sort of the P = M*topk flat pair
+ * indices f = t*topk + j by expert id:
+ *   expert_offsets [E+1]  exclusive prefix sum of the padded counts
+ *                         q_e = ceil(c_e / block_m) * block_m (0 if c_e = 0).
+ *   sorted_pair_ids [cap] expert e's pairs at [offsets[e], offsets[e]+c_e)
+ *                         in ascending f, then the sentinel P up to
+ *                         offsets[e+1].  Entries at or past *num_padded are
+ *                         unspecified.  cap = moe_align_capacity(...).
+ *   block_expert_ids [cap / block_m]  expert of each block_m-row block
+ *                         (defined for blocks below *num_padded / block_m).
+ *   pair_pos [P]          position of pair f in sorted_pair_ids; -1 for a
+ *                         pair whose id lies outside [0, E) (such pairs are
+ *                         dropped from every segment).
+ *   num_padded [1]        sum of q_e.
+ * All outputs are device int32 buffers; topk_ids is device int32 [M, topk].
+ * workspace: device, >= moe_workspace_size() bytes for a problem with these
+ * M, topk, E, block_m (it may be NULL when M*topk <= 1024).  The result is
+ * identical on every run.  M == 0 still writes expert_offsets (all 0) and
+ * num_padded (0).
+ */
+moe_status moe_align_permute(const int32_t* topk_ids, int32_t M, int32_t topk,
+                             int32_t E, int32_t block_m,
+                             int32_t* sorted_pair_ids,
+                             int32_t* block_expert_ids,
+                             int32_t* expert_offsets, int32_t* pair_pos,
+                             int32_t* num_padded, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * Expert computation and weighted combine.  For each real pair (t, j) with
+ * e = expert of the pair:
+ *   g = x_t . w13[e, 0:N]^T,  u = x_t . w13[e, N:2N]^T,  h = SiLU(g) * u,
+ *   y = h . w2[e]^T,          out[t] = sum_j topk_weights[t, j] * y
+ * with SiLU(z) = z / (1 + exp(-z)), fp32 accumulation, h held in bf16
+ * (bf16/f32 weights) or fp32 (E4M3 weights), the routing weight applied in
+ * the fp32 epilogue of the down projection, and one bf16/f32 rounding of out.
+ *
+ * FP8 (w_dtype == MOE_FP8_E4M3), per-tensor scaling ([post], "Backend routing
+ * for FP8 tensor quantization"; E4M3 named in "Amazon SageMaker AI 上的 MoE
+ * 内核工程优化实践", "Triton 后端路由"):
+ *   s_x = a1_scale ? *a1_scale : fl32(amax|x| / 448)  (1 if amax == 0),
+ *   x codes = E4M3(fl32(x / s_x)), round to nearest even, saturating;
+ *   GEMM1 output scaled by s_x * w13_scale[e];
+ *   s_h = a2_scale ? *a2_scale : fl32(amax|h| / 448) over all real pairs,
+ *   h codes = E4M3(fl32(h * fl32(1 / s_h)));
+ *   GEMM2 output scaled by s_h * w2_scale[e].
+ *
+ * a      device [M, K] of a_dtype.       w13  device [E, 2N, K] of w_dtype.
+ * w2     device [E, K, N] of w_dtype.    out  device [M, K] of out_dtype
+ *        (must not alias any input).
+ * w13_scale, w2_scale  device f32 [E]; required for E4M3 weights, else NULL.
+ * a1_scale, a2_scale   device f32 [1] static scales or NULL (dynamic); only
+ *        read for E4M3 weights.
+ * topk_weights         device f32 [M, topk] from moe_route_topk.
+ * sorted_pair_ids, block_expert_ids, expert_offsets, pair_pos, num_padded
+ *        device int32, from moe_align_permute with the same M, topk, E and
+ *        p->block_m.
+ * workspace            device, >= moe_workspace_size(p) bytes.
+ */
+moe_status moe_fused_forward(
+    const moe_problem* p, const void* a, const void* w13, const void* w2,
+    const float* w13_scale, const float* w2_scale, const float* a1_scale,
+    const float* a2_scale, const float* topk_weights,
+    const int32_t* sorted_pair_ids, const int32_t* block_expert_ids,
+    const int32_t* expert_offsets, const int32_t* pair_pos,
+    const int32_t* num_padded, void* out, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+/*
+ * FP8 activation quantisation on its own (the step moe_fused_forward runs
+ * first for E4M3 weights; exposed so that callers can pre-quantise and tests
+ * can check the codes bit for bit).  Per-tensor scaling as in [post],
+ * "Backend routing for FP8 tensor quantization":
+ *   *scale = static_scale ? *static_scale : fl32(amax|x| / 448) (1 if 0);
+ *   codes[i] = E4M3(fl32(x[i] / *scale)), IEEE fp32 division, round to
+ *   nearest even, saturating at +-448 (OCP E4M3FN).
+ * x          device [n] of x_dtype (MOE_F32 or MOE_BF16), 16-byte aligned.
+ * n          element count, a multiple of 128, >= 0.
+ * codes      device uint8 [n] (written), 16-byte aligned.
+ * scale      device f32 [1] (written).
+ * workspace  device, >= MOE_QUANT_WORKSPACE_BYTES bytes, 16-byte aligned.
+ */
+#define MOE_QUANT_WORKSPACE_BYTES 8192
+moe_status moe_quantize_act(const void* x, int32_t x_dtype, int64_t n,
+                            const float* static_scale, uint8_t* codes,
+                            float* scale, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * Measurement hook.  When set, the next moe_fused_forward call on this
+ * thread records events[0]/events[1] (hipEvent_t) on its stream right
+ * before and after the gate/up GEMM kernel, and events[2]/events[3] around
+ * the down GEMM (and, for M > 64, the combine kernel); the hook is then
+ * cleared.  NULL entries are skipped.  Host only; no effect on results.
+ */
+void moe_set_profile_events(void* const events[4]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,216 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of the fused MoE
+// layer: number formats, 16-byte memory access, wave reductions and the two
+// MFMA operand families (bf16 16x16x32 and E4M3 16x16x128).
+//
+// MFMA lane layout used throughout (CDNA3/CDNA4 16x16 family, wave64):
+//   operand A (16 rows x Kb):  lane l holds row (l % 16), K-group (l / 16);
+//   operand B (Kb x 16 cols):  lane l holds col (l % 16), K-group (l / 16);
+//   result C (16 x 16, fp32):  lane l holds C[4*(l/16) + i][l % 16], i = 0..3.
+// A K-group is 8 bf16 or 32 E4M3 values.  Which K indices a group holds is
+// the kernels' choice, as long as A and B use the same assignment (the sum
+// over K does not depend on its order): every kernel gives lane group g a
+// contiguous run of K so that each lane reads 32 contiguous bytes of a row.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------ number formats
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// binary32 -> bfloat16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// binary32 -> OCP E4M3FN code: round to nearest even, saturate to +-448,
+// NaN -> 0x7F.  Normal E4M3 values have 3 fraction bits, so rounding the
+// binary32 significand to 3 bits (ties to even) and rebasing the exponent
+// from bias 127 to bias 7 gives the code; below 2^-6 the spacing is a fixed
+// 2^-9, so the code is rint(|f| * 2^9).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = __builtin_fabsf(f);
+  if (!(a == a)) return 0x7fu;
+  if (a >= 448.0f) return sign | 0x7eu;
+  if (a < 0.015625f) return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+  uint32_t ua = __float_as_uint(a);
+  uint32_t r = (ua + 0x7ffffu + ((ua >> 20) & 1u)) & 0xfff00000u;
+  uint32_t e = ((r >> 23) & 0xffu) - 120u;  // (exp - 127) + 7
+  return sign | (e << 3) | ((r >> 20) & 7u);
+}
+
+// ----------------------------------------------------------------- memory
+
+__device__ __forceinline__ i32x4 ld16(const void* p) {
+  return *reinterpret_cast<const i32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, i32x4 v) {
+  *reinterpret_cast<i32x4*>(p) = v;
+}
+
+// ------------------------------------------------------------ wave helpers
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
+  return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Index of the s-th (0-based) expert with a non-empty segment, scanning
+// expert_offsets [E+1]; -1 if fewer than s+1 experts are active.  Every lane
+// of the calling wave gets the same answer.
+__device__ __forceinline__ int nth_active_expert(const int32_t* __restrict__ off,
+                                                 int E, int s) {
+  const int lane = threadIdx.x & 63;
+  int seen = 0;
+  for (int base = 0; base < E; base += kWave) {
+    int e = base + lane;
+    bool act = (e < E) && (off[e + 1] > off[e]);
+    uint64_t bal = __ballot(act);
+    int cnt = __popcll(bal);
+    if (s < seen + cnt) {
+      int want = s - seen;  // the want-th set bit of bal
+      int rank = __popcll(bal & lanemask_lt(lane));
+      uint64_t hit = __ballot(act && rank == want);
+      return base + __ffsll((long long)hit) - 1;
+    }
+    seen += cnt;
+  }
+  return -1;
+}
+
+// --------------------------------------------------- MFMA operand families
+//
+// One "step" is the part of K that one MFMA issue group consumes while each
+// lane reads 32 contiguous bytes of its row:
+//   bf16 family: 16 values per lane -> two 16x16x32 MFMAs, step = 64 of K;
+//   E4M3 family: 32 codes per lane  -> one 16x16x128 MFMA,  step = 128 of K.
+
+struct OpBF {
+  bf16x8 v[2];
+};
+struct OpF8 {
+  i32x8 v;
+};
+
+template <int SRC>
+struct Family;  // SRC = storage dtype of the operand in memory
+template <>
+struct Family<DT_BF16> {
+  using Op = OpBF;
+  static constexpr int kPerLane = 16;  // K values per lane per step
+  static constexpr int kBytes = 2;     // storage bytes per value
+};
+template <>
+struct Family<DT_F32> {
+  using Op = OpBF;
+  static constexpr int kPerLane = 16;
+  static constexpr int kBytes = 4;
+};
+template <>
+struct Family<DT_E4M3> {
+  using Op = OpF8;
+  static constexpr int kPerLane = 32;
+  static constexpr int kBytes = 1;
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(i32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// 8 fp32 -> 8 bf16 (round to nearest even) packed in an i32x4.
+__device__ __forceinline__ i32x4 pack_bf16x8(i32x4 a, i32x4 b) {
+  i32x4 r;
+  r[0] = (int)(f32_to_bf16_bits(__int_as_float(a[0])) | (f32_to_bf16_bits(__int_as_float(a[1])) << 16));
+  r[1] = (int)(f32_to_bf16_bits(__int_as_float(a[2])) | (f32_to_bf16_bits(__int_as_float(a[3])) << 16));
+  r[2] = (int)(f32_to_bf16_bits(__int_as_float(b[0])) | (f32_to_bf16_bits(__int_as_float(b[1])) << 16));
+  r[3] = (int)(f32_to_bf16_bits(__int_as_float(b[2])) | (f32_to_bf16_bits(__int_as_float(b[3])) << 16));
+  return r;
+}
+
+// Raw 32 bytes (two or four 16-byte loads) of one lane's step.
+template <int SRC>
+struct Raw {
+  i32x4 q[Family<SRC>::kPerLane * Family<SRC>::kBytes / 16];
+};
+
+template <int SRC>
+__device__ __forceinline__ Raw<SRC> load_raw(const void* p) {
+  Raw<SRC> r;
+  const char* c = reinterpret_cast<const char*>(p);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(r.q) / 16); ++i) r.q[i] = ld16(c + 16 * i);
+  return r;
+}
+
+template <int SRC>
+__device__ __forceinline__ typename Family<SRC>::Op to_op(const Raw<SRC>& r);
+
+template <>
+__device__ __forceinline__ OpBF to_op<DT_BF16>(const Raw<DT_BF16>& r) {
+  OpBF o;
+  o.v[0] = as_bf16x8(r.q[0]);
+  o.v[1] = as_bf16x8(r.q[1]);
+  return o;
+}
+template <>
+__device__ __forceinline__ OpBF to_op<DT_F32>(const Raw<DT_F32>& r) {
+  OpBF o;
+  o.v[0] = as_bf16x8(pack_bf16x8(r.q[0], r.q[1]));
+  o.v[1] = as_bf16x8(pack_bf16x8(r.q[2], r.q[3]));
+  return o;
+}
+template <>
+__device__ __forceinline__ OpF8 to_op<DT_E4M3>(const Raw<DT_E4M3>& r) {
+  OpF8 o;
+  o.v = i32x8{r.q[0][0], r.q[0][1], r.q[0][2], r.q[0][3],
+              r.q[1][0], r.q[1][1], r.q[1][2], r.q[1][3]};
+  return o;
+}
+
+__device__ __forceinline__ f32x4 mma(const OpBF& a, const OpBF& b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[0], b.v[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[1], b.v[1], c, 0, 0, 0);
+  return c;
+}
+__device__ __forceinline__ f32x4 mma(const OpF8& a, const OpF8& b, f32x4 c) {
+  // format code 0 = E4M3 for both operands; zero scale operands select the
+  // unscaled v_mfma_f32_16x16x128_f8f6f4.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.v, b.v, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+}  // namespace moe

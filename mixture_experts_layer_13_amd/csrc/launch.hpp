@@ -1,0 +1,65 @@
+// launch.hpp -- host-side launchers of the gfx950 kernels (internal to the
+// library; the public interface is include/moe.h).  Each returns 0 or the
+// hipError_t of the failed launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxPartials = 1024;
+
+int launch_route_topk(const float* logits, int M, int E, int k, int renorm,
+                      int32_t* ids, float* wts, hipStream_t stream);
+
+size_t align_workspace_bytes(int M, int topk, int E);
+int launch_align(const int32_t* ids, int M, int topk, int E, int bm,
+                 int32_t* sorted_ids, int32_t* block_expert, int32_t* offsets,
+                 int32_t* pair_pos, int32_t* num_padded, void* ws,
+                 hipStream_t stream);
+
+int launch_quant_x(const void* x, int xt, size_t n, const float* static_scale,
+                   float* partials, uint8_t* xq, float* sx, uint32_t* hmax_bits,
+                   hipStream_t stream);
+int launch_quant_h(const float* h32, int N, int max_rows, const int32_t* num_rows,
+                   const uint32_t* hmax_bits, const float* static_scale,
+                   uint8_t* hq, float* sh, hipStream_t stream);
+
+// Arguments of the expert GEMMs (device pointers unless noted).
+struct GemmArgs {
+  int M, K, N, E, topk, block_m, P;  // host values
+  int max_blocks;                    // host upper bound of padded blocks
+  int wt, xt, ot;                    // dtype codes (DT_*)
+  const void* x;        // activations for GEMM1 (bf16, f32 or E4M3 codes)
+  const void* w13;
+  const void* w2;
+  const float* w13_scale;
+  const float* w2_scale;
+  const float* sx;       // E4M3 only: scale of x (device scalar)
+  const float* sh;       // E4M3 only: scale of h (device scalar)
+  const float* topk_w;
+  const int32_t* sorted_ids;
+  const int32_t* block_expert;
+  const int32_t* offsets;
+  const int32_t* pair_pos;
+  const int32_t* num_padded;
+  void* h;               // [cap, N] bf16 (bf16 family) or fp32 (E4M3)
+  const void* hq;        // GEMM2 operand: h itself (bf16) or its E4M3 codes
+  uint32_t* hmax_bits;   // E4M3: running max |h|
+  float* y;              // tile path: [cap, K] fp32 weighted expert outputs
+  void* out;             // [M, K]
+};
+
+int launch_gemm1_stream(const GemmArgs& a, hipStream_t stream);
+int launch_gemm2_stream(const GemmArgs& a, hipStream_t stream);
+int launch_gemm1_tile(const GemmArgs& a, hipStream_t stream);
+int launch_gemm2_tile(const GemmArgs& a, hipStream_t stream);
+int launch_combine(const GemmArgs& a, hipStream_t stream);
+int launch_cast_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t stream);
+
+// Largest M served by the streaming (decode) kernels.
+constexpr int kStreamMaxM = 64;
+
+}  // namespace moe

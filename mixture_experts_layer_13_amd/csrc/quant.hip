@@ -1,0 +1,187 @@
+// quant.hip -- FP8 per-tensor activation scaling for E4M3 expert weights.
+//
+// "Amazon SageMaker AI 上的 Mixture-of-Experts 内核工程优化", section "Backend
+// routing for FP8 tensor quantization", covers FP8 per-tensor ("tensor-
+// quantized") MoE models; E4M3 (4 exponent, 3 mantissa bits) is named in
+// "Amazon SageMaker AI 上的 MoE 内核工程优化实践", section "Triton 后端路由".
+// The pages give no formula; the layer uses s = fl32(amax / 448) (1 when
+// amax = 0) and codes E4M3(fl32(v / s)), round to nearest even, saturating.
+//
+//   amax_partial_kernel: per-workgroup max |x| -> partials[g]; workgroup 0
+//     also clears the running max of |h| that the gate/up GEMM raises.
+//   quant_x_kernel: reduces the partials (or the whole tensor when launched
+//     as one workgroup), writes s_x and the E4M3 codes of x.
+//   quant_h_kernel: s_h from the running max (or a static scale), codes of
+//     the fp32 intermediate with the reciprocal multiply fl32(h * fl32(1/s_h)).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+constexpr int kQThreads = 256;
+
+template <int XT>
+__device__ __forceinline__ void load8(const void* x, size_t i, float v[8]) {
+  if (XT == DT_BF16) {
+    i32x4 q = ld16(reinterpret_cast<const uint16_t*>(x) + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bf16_bits_to_f32((uint32_t)q[j] & 0xffffu);
+      v[2 * j + 1] = bf16_bits_to_f32((uint32_t)q[j] >> 16);
+    }
+  } else {
+    i32x4 a = ld16(reinterpret_cast<const float*>(x) + i);
+    i32x4 b = ld16(reinterpret_cast<const float*>(x) + i + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = __int_as_float(a[j]);
+      v[4 + j] = __int_as_float(b[j]);
+    }
+  }
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < kQThreads / kWave; ++i) r = fmaxf(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+template <int XT>
+__global__ __launch_bounds__(kQThreads) void amax_partial_kernel(
+    const void* __restrict__ x, size_t n, float* __restrict__ partials,
+    uint32_t* __restrict__ hmax_bits) {
+  __shared__ float red[kQThreads / kWave];
+  float m = 0.0f;
+  for (size_t i = ((size_t)blockIdx.x * kQThreads + threadIdx.x) * 8; i < n;
+       i += (size_t)gridDim.x * kQThreads * 8) {
+    float v[8];
+    load8<XT>(x, i, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
+  }
+  m = block_max(m, red);
+  if (threadIdx.x == 0) {
+    partials[blockIdx.x] = m;
+    if (blockIdx.x == 0) *hmax_bits = 0u;
+  }
+}
+
+// nparts == 0: this is a single-workgroup launch that reduces x itself.
+template <int XT>
+__global__ __launch_bounds__(kQThreads) void quant_x_kernel(
+    const void* __restrict__ x, size_t n, const float* __restrict__ partials,
+    int nparts, const float* __restrict__ static_scale, uint8_t* __restrict__ xq,
+    float* __restrict__ sx_out, uint32_t* __restrict__ hmax_bits) {
+  __shared__ float red[kQThreads / kWave];
+  float s;
+  if (static_scale) {
+    s = *static_scale;
+  } else {
+    float m = 0.0f;
+    if (nparts == 0) {
+      for (size_t i = (size_t)threadIdx.x * 8; i < n; i += kQThreads * 8) {
+        float v[8];
+        load8<XT>(x, i, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
+      }
+    } else {
+      for (int i = threadIdx.x; i < nparts; i += kQThreads) m = fmaxf(m, partials[i]);
+    }
+    m = block_max(m, red);
+    s = (m == 0.0f) ? 1.0f : m / 448.0f;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *sx_out = s;
+    if (nparts == 0) *hmax_bits = 0u;
+  }
+  for (size_t i = ((size_t)blockIdx.x * kQThreads + threadIdx.x) * 8; i < n;
+       i += (size_t)gridDim.x * kQThreads * 8) {
+    float v[8];
+    load8<XT>(x, i, v);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(v[j] / s) << (8 * j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hi |= f32_to_e4m3(v[4 + j] / s) << (8 * j);
+    *reinterpret_cast<uint2*>(xq + i) = make_uint2(lo, hi);
+  }
+}
+
+// h32: [rows, N] fp32; codes for rows < *num_rows.
+__global__ __launch_bounds__(kQThreads) void quant_h_kernel(
+    const float* __restrict__ h32, int N, const int32_t* __restrict__ num_rows,
+    const uint32_t* __restrict__ hmax_bits, const float* __restrict__ static_scale,
+    uint8_t* __restrict__ hq, float* __restrict__ sh_out) {
+  float s;
+  if (static_scale) {
+    s = *static_scale;
+  } else {
+    float m = __uint_as_float(*hmax_bits);
+    s = (m == 0.0f) ? 1.0f : m / 448.0f;
+  }
+  const float r = 1.0f / s;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *sh_out = s;
+  const size_t n = (size_t)(*num_rows) * N;
+  for (size_t i = ((size_t)blockIdx.x * kQThreads + threadIdx.x) * 8; i < n;
+       i += (size_t)gridDim.x * kQThreads * 8) {
+    i32x4 a = ld16(h32 + i), b = ld16(h32 + i + 4);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(__int_as_float(a[j]) * r) << (8 * j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hi |= f32_to_e4m3(__int_as_float(b[j]) * r) << (8 * j);
+    *reinterpret_cast<uint2*>(hq + i) = make_uint2(lo, hi);
+  }
+}
+
+int launch_quant_x(const void* x, int xt, size_t n, const float* static_scale,
+                   float* partials, uint8_t* xq, float* sx, uint32_t* hmax_bits,
+                   hipStream_t stream) {
+  // n is a multiple of 128 (K % 128 == 0).
+  const size_t per_wg = (size_t)kQThreads * 8;
+  size_t want = (n + per_wg - 1) / per_wg;
+  if (n <= (size_t)1 << 16 || static_scale) {
+    // one workgroup reduces and quantises (small tensors), or no reduction
+    int g = static_scale ? (int)(want < 1024 ? (want ? want : 1) : 1024) : 1;
+    if (xt == DT_BF16)
+      hipLaunchKernelGGL(quant_x_kernel<DT_BF16>, dim3(g), dim3(kQThreads), 0, stream,
+                         x, n, partials, 0, static_scale, xq, sx, hmax_bits);
+    else
+      hipLaunchKernelGGL(quant_x_kernel<DT_F32>, dim3(g), dim3(kQThreads), 0, stream,
+                         x, n, partials, 0, static_scale, xq, sx, hmax_bits);
+    return (int)hipGetLastError();
+  }
+  int g = (int)(want < kMaxPartials ? want : kMaxPartials);
+  if (xt == DT_BF16) {
+    hipLaunchKernelGGL(amax_partial_kernel<DT_BF16>, dim3(g), dim3(kQThreads), 0, stream,
+                       x, n, partials, hmax_bits);
+    hipLaunchKernelGGL(quant_x_kernel<DT_BF16>, dim3(g), dim3(kQThreads), 0, stream,
+                       x, n, partials, g, nullptr, xq, sx, hmax_bits);
+  } else {
+    hipLaunchKernelGGL(amax_partial_kernel<DT_F32>, dim3(g), dim3(kQThreads), 0, stream,
+                       x, n, partials, hmax_bits);
+    hipLaunchKernelGGL(quant_x_kernel<DT_F32>, dim3(g), dim3(kQThreads), 0, stream,
+                       x, n, partials, g, nullptr, xq, sx, hmax_bits);
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_quant_h(const float* h32, int N, int max_rows, const int32_t* num_rows,
+                   const uint32_t* hmax_bits, const float* static_scale, uint8_t* hq,
+                   float* sh, hipStream_t stream) {
+  size_t n = (size_t)max_rows * N;
+  const size_t per_wg = (size_t)kQThreads * 8;
+  size_t want = (n + per_wg - 1) / per_wg;
+  int g = (int)(want < 2048 ? (want ? want : 1) : 2048);
+  hipLaunchKernelGGL(quant_h_kernel, dim3(g), dim3(kQThreads), 0, stream, h32, N,
+                     num_rows, hmax_bits, static_scale, hq, sh);
+  return (int)hipGetLastError();
+}
+
+}  // namespace moe

@@ -82,7 +82,14 @@ double oracle_e4m3_to_f64(uint8_t b) {
 /* Nearest E4M3FN code to a binary32 value: search every finite magnitude
  * code, keep the closest; on an exact tie keep the even code (round half to
  * even).  Magnitudes at or beyond 448 saturate to 448.  NaN maps to 0x7F. */
+static double g_e4m3_mag[0x7F];
+static int g_e4m3_ready = 0;
+
 uint8_t oracle_e4m3_from_f32(float f) {
+  if (!g_e4m3_ready) { /* magnitudes of codes 0x00..0x7E (idempotent fill) */
+    for (int c = 0; c < 0x7F; ++c) g_e4m3_mag[c] = oracle_e4m3_to_f64((uint8_t)c);
+    g_e4m3_ready = 1;
+  }
   if (isnan(f)) return 0x7F;
   uint8_t sign = signbit(f) ? 0x80 : 0x00;
   double a = fabs((double)f);
@@ -90,7 +97,7 @@ uint8_t oracle_e4m3_from_f32(float f) {
   int best = 0;
   double best_d = a; /* distance to code 0 */
   for (int c = 1; c <= 0x7E; ++c) {
-    double d = fabs(a - oracle_e4m3_to_f64((uint8_t)c));
+    double d = fabs(a - g_e4m3_mag[c]);
     if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
       best = c;
       best_d = d;
@@ -285,13 +292,20 @@ int oracle_moe_forward(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
   if (!xd) return 2;
   float sx = 1.0f;
   if (fp8_act) {
+    /* the scale spans all of x; rows are quantised where they are used */
     sx = a1_scale ? *a1_scale : oracle_act_scale(x_dtype, x, T * (int64_t)H);
-    uint8_t* q = (uint8_t*)malloc((size_t)(T * (int64_t)H + 1));
-    if (!q) return 2;
-    oracle_quantize_e4m3(x_dtype, x, T * (int64_t)H, sx, q);
-    for (int64_t i = 0; i < T * (int64_t)H; ++i)
-      xd[i] = (double)sx * oracle_e4m3_to_f64(q[i]);
-    free(q);
+    int need_all = !a2_scale || !tokens;
+    (void)oracle_e4m3_from_f32(0.0f); /* fill the code table before threads */
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      int used = need_all;
+      for (int64_t q = 0; !used && q < n_tokens; ++q) used = (tokens[q] == t);
+      if (!used) continue;
+      for (int32_t h = 0; h < H; ++h) {
+        float v = (float)load_elem(x_dtype, x, t * H + h);
+        xd[t * H + h] = (double)sx * oracle_e4m3_to_f64(oracle_e4m3_from_f32(v / sx));
+      }
+    }
   } else {
     for (int64_t i = 0; i < T * (int64_t)H; ++i)
       xd[i] = load_elem(x_dtype, x, i);
