@@ -111,6 +111,19 @@ __device__ __forceinline__ int nth_active_expert(const int32_t* __restrict__ off
   return -1;
 }
 
+// Count the real (non-sentinel) entries of an expert segment; sentinels sit
+// only at the tail, so this is also the index of the first padding slot.
+__device__ __forceinline__ int segment_count(const int32_t* __restrict__ sorted_ids,
+                                             int seg0, int seg1, int P) {
+  const int lane = threadIdx.x & 63;
+  int cnt = 0;
+  for (int s = seg0; s < seg1; s += kWave) {
+    bool real = (s + lane < seg1) && (sorted_ids[s + lane] < P);
+    cnt += __popcll(__ballot(real));
+  }
+  return cnt;
+}
+
 // --------------------------------------------------- MFMA operand families
 //
 // One "step" is the part of K that one MFMA issue group consumes while each
@@ -172,6 +185,25 @@ __device__ __forceinline__ Raw<SRC> load_raw(const void* p) {
   const char* c = reinterpret_cast<const char*>(p);
 #pragma unroll
   for (int i = 0; i < (int)(sizeof(r.q) / 16); ++i) r.q[i] = ld16(c + 16 * i);
+  return r;
+}
+
+// Streaming variant for data read exactly once (expert weights): non-temporal
+// loads keep it from displacing reusable lines (activations, h) in L2.
+template <int SRC>
+__device__ __forceinline__ Raw<SRC> load_raw_nt(const void* p) {
+  Raw<SRC> r;
+  const i32x4* c = reinterpret_cast<const i32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(r.q) / 16); ++i) r.q[i] = __builtin_nontemporal_load(c + i);
+  return r;
+}
+
+template <int SRC>
+__device__ __forceinline__ Raw<SRC> zero_raw() {
+  Raw<SRC> r;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(r.q) / 16); ++i) r.q[i] = i32x4{0, 0, 0, 0};
   return r;
 }
 

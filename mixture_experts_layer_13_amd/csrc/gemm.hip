@@ -42,56 +42,79 @@ constexpr int lane_bytes() {
   return Family<T>::kPerLane * Family<T>::kBytes;  // bytes per lane per step
 }
 
-// Count the real (non-sentinel) entries of an expert segment; sentinels sit
-// only at the tail, so this is also the index of the first padding slot.
-__device__ __forceinline__ int segment_count(const int32_t* __restrict__ sorted_ids,
-                                             int seg0, int seg1, int P) {
-  const int lane = threadIdx.x & 63;
-  int cnt = 0;
-  for (int s = seg0; s < seg1; s += kWave) {
-    bool real = (s + lane < seg1) && (sorted_ids[s + lane] < P);
-    cnt += __popcll(__ballot(real));
-  }
-  return cnt;
-}
 
 template <int OT>
 __device__ __forceinline__ void store_out4(void* out, size_t idx, const float v[4]);
 
 // ======================================================== stream: gate/up
+//
+// The K loop of both stream kernels is software-pipelined in registers: a
+// wave holds two groups of U steps and issues the loads of the next group
+// before the MFMAs of the current one, so about 2U steps of weight rows stay
+// in flight per wave without waiting on the arithmetic.
 
 constexpr int kG1Waves = 4;
+constexpr int kG1Unroll1 = 2;      // K steps per group, one 16-token column block
+constexpr int kG1Unroll2 = 1;      // K steps per group, two column blocks
+constexpr int kG2Unroll1 = 2;      // down GEMM, one column block
+constexpr int kG2Unroll2 = 2;      // down GEMM, two column blocks
+constexpr int kStreamMaxNcb = 2;   // column blocks per pass (more tokens: more passes)
+constexpr bool kNtWeights = false; // non-temporal expert-weight loads (slower here)
+
+template <int SRC>
+__device__ __forceinline__ Raw<SRC> load_w(const void* p) {
+  if constexpr (kNtWeights) return load_raw_nt<SRC>(p);
+  else return load_raw<SRC>(p);
+}
 
 template <int WT, int XT, int NCB, int U>
-__device__ __forceinline__ void g1_stream_steps(const char* wg, const char* wu,
-                                                const char* const xr[NCB], int s,
-                                                int ncb, f32x4 accg[NCB],
-                                                f32x4 accu[NCB]) {
+struct G1Group {
+  Raw<WT> g[U], u[U];
+  Raw<XT> x[U][NCB];
+};
+
+// Loads steps s, s + stride, ... (U of them, those below nsteps).
+template <int WT, int XT, int NCB, int U>
+__device__ __forceinline__ void g1_load(G1Group<WT, XT, NCB, U>& G, const char* wg,
+                                        const char* wu, const char* const xr[NCB],
+                                        const bool xv[NCB], int s, int stride, int nsteps,
+                                        int ncb) {
   constexpr int SB_W = fam_step<WT>() * Family<WT>::kBytes;  // bytes per step (row)
   constexpr int SB_X = fam_step<XT>() * Family<XT>::kBytes;
-  Raw<WT> rg[U], ru[U];
-  Raw<XT> rx[U][NCB];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const size_t o = (size_t)(s + kG1Waves * u) * SB_W;
-    rg[u] = load_raw<WT>(wg + o);
-    ru[u] = load_raw<WT>(wu + o);
+    const int st = s + stride * u;
+    if (st < nsteps) {
+      G.g[u] = load_w<WT>(wg + (size_t)st * SB_W);
+      G.u[u] = load_w<WT>(wu + (size_t)st * SB_W);
+    }
   }
+  // token rows past the expert's count contribute nothing: no load, zeros
 #pragma unroll
-  for (int u = 0; u < U; ++u)
+  for (int u = 0; u < U; ++u) {
+    const int st = s + stride * u;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
-      if (cb < ncb) rx[u][cb] = load_raw<XT>(xr[cb] + (size_t)(s + kG1Waves * u) * SB_X);
+      if (st < nsteps && cb < ncb)
+        G.x[u][cb] = xv[cb] ? load_raw<XT>(xr[cb] + (size_t)st * SB_X) : zero_raw<XT>();
+  }
+}
+
+template <int WT, int XT, int NCB, int U>
+__device__ __forceinline__ void g1_mma(const G1Group<WT, XT, NCB, U>& G, int s, int stride,
+                                       int nsteps, int ncb, f32x4 accg[NCB], f32x4 accu[NCB]) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    auto ag = to_op<WT>(rg[u]);
-    auto au = to_op<WT>(ru[u]);
+    if (s + stride * u < nsteps) {
+      auto ag = to_op<WT>(G.g[u]);
+      auto au = to_op<WT>(G.u[u]);
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      if (cb < ncb) {
-        auto b = to_op<XT>(rx[u][cb]);
-        accg[cb] = mma(ag, b, accg[cb]);
-        accu[cb] = mma(au, b, accu[cb]);
+      for (int cb = 0; cb < NCB; ++cb) {
+        if (cb < ncb) {
+          auto b = to_op<XT>(G.x[u][cb]);
+          accg[cb] = mma(ag, b, accg[cb]);
+          accu[cb] = mma(au, b, accu[cb]);
+        }
       }
     }
   }
@@ -99,7 +122,7 @@ __device__ __forceinline__ void g1_stream_steps(const char* wg, const char* wu,
 
 template <int WT, int XT, int NCB>
 __global__ __launch_bounds__(256) void gemm1_stream_kernel(GemmArgs a) {
-  constexpr int U = (NCB <= 2) ? 4 : 2;
+  constexpr int U = (NCB == 1) ? kG1Unroll1 : kG1Unroll2;
   __shared__ float red[kG1Waves][2][NCB][4][kWave];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
@@ -125,21 +148,35 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(GemmArgs a) {
   for (int c0 = 0; c0 < me; c0 += 16 * NCB) {
     const int ncb = min(NCB, (me - c0 + 15) / 16);
     const char* xr[NCB];
+    bool xv[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       int col = c0 + cb * 16 + r16;
-      int f = (col < me) ? a.sorted_ids[seg0 + col] : a.sorted_ids[seg0];
+      xv[cb] = col < me;
+      int f = xv[cb] ? a.sorted_ids[seg0 + col] : a.sorted_ids[seg0];
       xr[cb] = xb + (size_t)(f / a.topk) * K * XB;
     }
     f32x4 accg[NCB], accu[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) accg[cb] = accu[cb] = f32x4{0, 0, 0, 0};
 
-    int s = wv;
-    for (; s + kG1Waves * (U - 1) < nsteps; s += kG1Waves * U)
-      g1_stream_steps<WT, XT, NCB, U>(wg, wu, xr, s, ncb, accg, accu);
-    for (; s < nsteps; s += kG1Waves)
-      g1_stream_steps<WT, XT, NCB, 1>(wg, wu, xr, s, ncb, accg, accu);
+    {
+      // wave wv takes steps wv, wv + 4, ...; groups of U steps, two in flight
+      constexpr int S = kG1Waves * U;
+      G1Group<WT, XT, NCB, U> A, B;
+      int s = wv;
+      g1_load(A, wg, wu, xr, xv, s, kG1Waves, nsteps, ncb);
+      while (true) {
+        if (s + S < nsteps) g1_load(B, wg, wu, xr, xv, s + S, kG1Waves, nsteps, ncb);
+        g1_mma(A, s, kG1Waves, nsteps, ncb, accg, accu);
+        s += S;
+        if (s >= nsteps) break;
+        if (s + S < nsteps) g1_load(A, wg, wu, xr, xv, s + S, kG1Waves, nsteps, ncb);
+        g1_mma(B, s, kG1Waves, nsteps, ncb, accg, accu);
+        s += S;
+        if (s >= nsteps) break;
+      }
+    }
 
     // reduce the 4 K-slices
 #pragma unroll
@@ -192,33 +229,49 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(GemmArgs a) {
 constexpr int kG2Waves = 8;
 
 template <int WT, int NCB, int U>
-__device__ __forceinline__ void g2_stream_steps(const char* wr, const char* const hr[NCB],
-                                                int s, int ncb, f32x4 acc[NCB]) {
-  constexpr int HT = (WT == DT_E4M3) ? DT_E4M3 : DT_BF16;
+struct G2Group {
+  static constexpr int HT = (WT == DT_E4M3) ? DT_E4M3 : DT_BF16;
+  Raw<WT> w[U];
+  Raw<HT> h[U][NCB];
+};
+
+template <int WT, int NCB, int U>
+__device__ __forceinline__ void g2_load(G2Group<WT, NCB, U>& G, const char* wr,
+                                        const char* const hr[NCB], const bool hv[NCB], int s,
+                                        int nsteps, int ncb) {
+  constexpr int HT = G2Group<WT, NCB, U>::HT;
   constexpr int SB_W = fam_step<WT>() * Family<WT>::kBytes;
   constexpr int SB_H = fam_step<HT>() * Family<HT>::kBytes;
-  Raw<WT> rw[U];
-  Raw<HT> rh[U][NCB];
 #pragma unroll
-  for (int u = 0; u < U; ++u) rw[u] = load_raw<WT>(wr + (size_t)(s + u) * SB_W);
+  for (int u = 0; u < U; ++u)
+    if (s + u < nsteps) G.w[u] = load_w<WT>(wr + (size_t)(s + u) * SB_W);
 #pragma unroll
   for (int u = 0; u < U; ++u)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
-      if (cb < ncb) rh[u][cb] = load_raw<HT>(hr[cb] + (size_t)(s + u) * SB_H);
+      if (s + u < nsteps && cb < ncb)
+        G.h[u][cb] = hv[cb] ? load_raw<HT>(hr[cb] + (size_t)(s + u) * SB_H) : zero_raw<HT>();
+}
+
+template <int WT, int NCB, int U>
+__device__ __forceinline__ void g2_mma(const G2Group<WT, NCB, U>& G, int s, int nsteps, int ncb,
+                                       f32x4 acc[NCB]) {
+  constexpr int HT = G2Group<WT, NCB, U>::HT;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    auto aw = to_op<WT>(rw[u]);
+    if (s + u < nsteps) {
+      auto aw = to_op<WT>(G.w[u]);
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-      if (cb < ncb) acc[cb] = mma(aw, to_op<HT>(rh[u][cb]), acc[cb]);
+      for (int cb = 0; cb < NCB; ++cb)
+        if (cb < ncb) acc[cb] = mma(aw, to_op<HT>(G.h[u][cb]), acc[cb]);
+    }
   }
 }
 
 template <int WT, int OT, int NCB>
 __global__ __launch_bounds__(512) void gemm2_stream_kernel(GemmArgs a) {
   constexpr int HT = (WT == DT_E4M3) ? DT_E4M3 : DT_BF16;
-  constexpr int U = (NCB <= 2) ? 4 : 2;
+  constexpr int U = (NCB == 1) ? kG2Unroll1 : kG2Unroll2;
   extern __shared__ float acc_lds[];  // [kG2Waves][M][16]
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
@@ -253,12 +306,14 @@ __global__ __launch_bounds__(512) void gemm2_stream_kernel(GemmArgs a) {
       for (int c0 = 0; c0 < me; c0 += 16 * NCB) {
         const int ncb = min(NCB, (me - c0 + 15) / 16);
         const char* hr[NCB];
+        bool hv[NCB];
         int tok[NCB];
         float rw[NCB];
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           int col = c0 + cb * 16 + r16;
           bool ok = col < me;
+          hv[cb] = ok;
           int pos = seg0 + (ok ? col : 0);
           int f = a.sorted_ids[pos];
           hr[cb] = hbase + (size_t)pos * N * HB;
@@ -268,9 +323,21 @@ __global__ __launch_bounds__(512) void gemm2_stream_kernel(GemmArgs a) {
         f32x4 acc[NCB];
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0, 0, 0, 0};
-        int s = 0;
-        for (; s + U <= nsteps; s += U) g2_stream_steps<WT, NCB, U>(wr, hr, s, ncb, acc);
-        for (; s < nsteps; ++s) g2_stream_steps<WT, NCB, 1>(wr, hr, s, ncb, acc);
+        {
+          G2Group<WT, NCB, U> A, B;
+          int s = 0;
+          g2_load(A, wr, hr, hv, s, nsteps, ncb);
+          while (true) {
+            if (s + U < nsteps) g2_load(B, wr, hr, hv, s + U, nsteps, ncb);
+            g2_mma(A, s, nsteps, ncb, acc);
+            s += U;
+            if (s >= nsteps) break;
+            if (s + U < nsteps) g2_load(A, wr, hr, hv, s + U, nsteps, ncb);
+            g2_mma(B, s, nsteps, ncb, acc);
+            s += U;
+            if (s >= nsteps) break;
+          }
+        }
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           if (cb < ncb && tok[cb] >= 0) {
@@ -574,17 +641,16 @@ __global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict_
 
 template <int WT, int XT>
 static int g1s_dispatch(const GemmArgs& a, hipStream_t st, dim3 grid) {
-  const int ncb = (min(a.M, kStreamMaxM) + 15) / 16;
+  const int ncb = min((min(a.M, kStreamMaxM) + 15) / 16, kStreamMaxNcb);
   if (ncb <= 1)
     hipLaunchKernelGGL((gemm1_stream_kernel<WT, XT, 1>), grid, dim3(256), 0, st, a);
-  else if (ncb <= 2)
-    hipLaunchKernelGGL((gemm1_stream_kernel<WT, XT, 2>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((gemm1_stream_kernel<WT, XT, 4>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm1_stream_kernel<WT, XT, kStreamMaxNcb>), grid, dim3(256), 0, st, a);
   return (int)hipGetLastError();
 }
 
 int launch_gemm1_stream(const GemmArgs& a, hipStream_t st) {
+  if (gemm1_ring_applies(a)) return launch_gemm1_ring(a, st);
   dim3 grid(a.N / 16, min(a.E, a.P));
   if (a.wt == DT_E4M3) return g1s_dispatch<DT_E4M3, DT_E4M3>(a, st, grid);
   if (a.wt == DT_BF16)
@@ -596,15 +662,13 @@ int launch_gemm1_stream(const GemmArgs& a, hipStream_t st) {
 
 template <int WT, int OT>
 static int g2s_dispatch(const GemmArgs& a, hipStream_t st) {
-  const int ncb = (min(a.M, kStreamMaxM) + 15) / 16;
+  const int ncb = min((min(a.M, kStreamMaxM) + 15) / 16, kStreamMaxNcb);
   dim3 grid(a.K / 16);
   size_t lds = (size_t)kG2Waves * a.M * 16 * sizeof(float);
   if (ncb <= 1)
     hipLaunchKernelGGL((gemm2_stream_kernel<WT, OT, 1>), grid, dim3(512), lds, st, a);
-  else if (ncb <= 2)
-    hipLaunchKernelGGL((gemm2_stream_kernel<WT, OT, 2>), grid, dim3(512), lds, st, a);
   else
-    hipLaunchKernelGGL((gemm2_stream_kernel<WT, OT, 4>), grid, dim3(512), lds, st, a);
+    hipLaunchKernelGGL((gemm2_stream_kernel<WT, OT, kStreamMaxNcb>), grid, dim3(512), lds, st, a);
   return (int)hipGetLastError();
 }
 

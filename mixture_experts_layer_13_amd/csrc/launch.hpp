@@ -53,6 +53,8 @@ struct GemmArgs {
 };
 
 int launch_gemm1_stream(const GemmArgs& a, hipStream_t stream);
+bool gemm1_ring_applies(const GemmArgs& a);
+int launch_gemm1_ring(const GemmArgs& a, hipStream_t stream);
 int launch_gemm2_stream(const GemmArgs& a, hipStream_t stream);
 int launch_gemm1_tile(const GemmArgs& a, hipStream_t stream);
 int launch_gemm2_tile(const GemmArgs& a, hipStream_t stream);
