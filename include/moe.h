@@ -149,6 +149,21 @@ moe_status moe_align_permute(const int32_t* topk_ids, int32_t M, int32_t topk,
                              size_t workspace_bytes, void* stream);
 
 /*
+ * moe_route_topk followed by moe_align_permute, with the same arguments and
+ * results as the two calls (bit for bit).  When M <= 16 and M*topk <= 1024
+ * both run in one workgroup of one launch (one token row per wave), the ids
+ * staying on chip between them; this is the small-decode case, where the
+ * fixed cost of a launch is a visible part of the layer's time.  Larger
+ * batches take the two-call path.
+ */
+moe_status moe_route_align(const float* logits, int32_t M, int32_t E, int32_t topk,
+                           int32_t renormalize, int32_t block_m, int32_t* topk_ids,
+                           float* topk_weights, int32_t* sorted_pair_ids,
+                           int32_t* block_expert_ids, int32_t* expert_offsets,
+                           int32_t* pair_pos, int32_t* num_padded, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
  * Expert computation and weighted combine.  For each real pair (t, j) with
  * e = expert of the pair:
  *   g = x_t . w13[e, 0:N]^T,  u = x_t . w13[e, N:2N]^T,  h = SiLU(g) * u,
@@ -213,7 +228,8 @@ moe_status moe_quantize_act(const void* x, int32_t x_dtype, int64_t n,
  * thread records events[0]/events[1] (hipEvent_t) on its stream right
  * before and after the gate/up GEMM kernel, and events[2]/events[3] around
  * the down GEMM (and, for M > 64, the combine kernel); the hook is then
- * cleared.  NULL entries are skipped.  Host only; no effect on results.
+ * cleared.  NULL entries are skipped.  Meant for eager (uncaptured)
+ * calls.  Host only; no effect on results.
  */
 void moe_set_profile_events(void* const events[4]);
 

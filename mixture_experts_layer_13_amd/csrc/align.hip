@@ -19,11 +19,10 @@
 //     spread over the chunks' waves.
 #include "common.hpp"
 #include "launch.hpp"
+#include "route_align.hpp"
 
 namespace moe {
 
-constexpr int kChunk = 1024;
-constexpr int kChunkWaves = kChunk / kWave;  // 16
 
 __global__ __launch_bounds__(kChunk) void align_hist_kernel(
     const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ hist) {
@@ -40,133 +39,44 @@ __global__ __launch_bounds__(kChunk) void align_hist_kernel(
     hist[(size_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// Exclusive scan of v over the whole workgroup (kChunk threads); returns the
-// prefix for this thread and writes the total to *total.
-__device__ int block_excl_scan(int v, int* wsum, int* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wsum[w] = x;
-  __syncthreads();
-  if (w == 0) {
-    int s = (lane < kChunkWaves) ? wsum[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int y = __shfl_up(s, o, kWave);
-      if (lane >= o) s += y;
-    }
-    if (lane < kChunkWaves) wsum[lane] = s;  // inclusive per wave
-  }
-  __syncthreads();
-  int before = (w == 0) ? 0 : wsum[w - 1];
-  *total = wsum[kChunkWaves - 1];
-  int r = before + x - v;
-  __syncthreads();  // wsum may be reused by the caller
-  return r;
-}
-
 __global__ __launch_bounds__(kChunk) void align_scatter_kernel(
     const int32_t* __restrict__ ids, int P, int E, int bm, int nchunks,
     const int32_t* __restrict__ hist, int32_t* __restrict__ sorted_ids,
     int32_t* __restrict__ block_expert, int32_t* __restrict__ offsets_out,
     int32_t* __restrict__ pair_pos, int32_t* __restrict__ num_padded) {
-  // LDS: total[E], base[E], off[E+1], wcnt[16][E+1], wsum[16]
   extern __shared__ int32_t sm[];
-  int32_t* total = sm;
-  int32_t* base = total + E;
-  int32_t* off = base + E;
-  int32_t* wcnt = off + (E + 1);
-  int32_t* wsum = wcnt + kChunkWaves * (E + 1);
-  __shared__ int32_t s_total;
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int c = blockIdx.x;
-
-  // 1. totals per expert and this chunk's base per expert
-  if (nchunks == 1) {
-    for (int e = tid; e < E; e += kChunk) {
-      total[e] = 0;
-      base[e] = 0;
-    }
-    __syncthreads();
-    int f = tid;
-    if (f < P) {
-      int id = ids[f];
-      if (id >= 0 && id < E) atomicAdd(&total[id], 1);
-    }
-  } else {
-    for (int e = tid; e < E; e += kChunk) {
-      int t = 0, b = 0;
-      for (int cc = 0; cc < nchunks; ++cc) {
-        int h = hist[(size_t)cc * E + e];
-        if (cc < c) b += h;
-        t += h;
-      }
-      total[e] = t;
-      base[e] = b;
-    }
-  }
-  for (int i = tid; i < kChunkWaves * (E + 1); i += kChunk) wcnt[i] = 0;
-  __syncthreads();
-
-  // 2. padded offsets (E <= 1024 = one value per thread)
-  int q = 0;
-  if (tid < E) q = (total[tid] + bm - 1) / bm * bm;
-  int tot;
-  int pre = block_excl_scan(q, wsum, &tot);
-  if (tid < E) off[tid] = pre;
-  if (tid == 0) {
-    off[E] = tot;
-    s_total = tot;
-  }
-  __syncthreads();
-  if (c == 0) {
-    for (int e = tid; e <= E; e += kChunk) offsets_out[e] = off[e];
-    if (tid == 0) *num_padded = s_total;
-  }
-
-  // 3. in-chunk rank among equal ids (ids outside [0,E) get key E: dropped)
-  const int f = c * kChunk + tid;
-  int key = 2047;  // lanes past P: a key no real pair has
-  if (f < P) {
-    int id = ids[f];
-    key = (id >= 0 && id < E) ? id : E;
-  }
-  uint64_t match = ~0ull;
-#pragma unroll
-  for (int b = 0; b < 11; ++b) {
-    uint64_t bal = __ballot((key >> b) & 1);
-    match &= ((key >> b) & 1) ? bal : ~bal;
-  }
-  const int in_wave = __popcll(match & lanemask_lt(lane));
-  const bool leader = in_wave == 0;
-  if (leader && key <= E) wcnt[w * (E + 1) + key] = __popcll(match);
-  __syncthreads();
-  if (f < P) {
-    if (key < E) {
-      int r = in_wave;
-      for (int ww = 0; ww < w; ++ww) r += wcnt[ww * (E + 1) + key];
-      int pos = off[key] + base[key] + r;
-      sorted_ids[pos] = f;
-      pair_pos[f] = pos;
-    } else {
-      pair_pos[f] = -1;
-    }
-  }
-
-  // 4. padding sentinels and block -> expert map; expert e is handled by
-  //    global wave (e mod (nchunks*16)).
-  const int gw = c * kChunkWaves + w, nw = nchunks * kChunkWaves;
-  for (int e = gw; e < E; e += nw) {
-    int s0 = off[e] + total[e], s1 = off[e + 1];
-    for (int s = s0 + lane; s < s1; s += kWave) sorted_ids[s] = P;
-    for (int b = off[e] / bm + lane; b < s1 / bm; b += kWave) block_expert[b] = e;
-  }
+  align_chunk(ids, P, E, bm, nchunks, blockIdx.x, hist, sorted_ids, block_expert, offsets_out,
+              pair_pos, num_padded, sm);
 }
+
+// Routing and alignment in one workgroup when all pairs fit one chunk (the
+// decode case): the ids stay in LDS between the two phases.
+template <int NPER>
+__global__ __launch_bounds__(kChunk) void route_align_kernel(
+    const float* __restrict__ logits, int M, int E, int k, int renorm, int bm,
+    int32_t* __restrict__ ids, float* __restrict__ wts, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ block_expert, int32_t* __restrict__ offsets_out,
+    int32_t* __restrict__ pair_pos, int32_t* __restrict__ num_padded) {
+  extern __shared__ int32_t sm[];
+  int32_t* lids = sm;             // [kChunk]
+  int32_t* scratch = sm + kChunk;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int row = w; row < M; row += kChunkWaves) {
+    int id;
+    float wt;
+    route_row<NPER>(logits + (size_t)row * E, E, k, renorm, lane, id, wt);
+    if (lane < k) {
+      ids[(size_t)row * k + lane] = id;
+      wts[(size_t)row * k + lane] = wt;
+      lids[row * k + lane] = id;
+    }
+  }
+  __syncthreads();
+  align_chunk(lids, M * k, E, bm, 1, 0, nullptr, sorted_ids, block_expert, offsets_out, pair_pos,
+              num_padded, scratch);
+}
+
+static size_t align_lds_bytes(int E);
 
 size_t align_workspace_bytes(int M, int topk, int E) {
   long long P = (long long)M * topk;
@@ -188,12 +98,12 @@ int launch_align(const int32_t* ids, int M, int topk, int E, int bm,
     int err = (int)hipGetLastError();
     if (err) return err;
   }
-  size_t lds = (size_t)(3 * E + 1 + kChunkWaves * (E + 1) + kChunkWaves) * 4;
+  size_t lds = align_lds_bytes(E);
   static bool attr_set = false;  // E = 1024 needs ~78 KiB of the 160 KiB LDS
   if (!attr_set) {
     int err = (int)hipFuncSetAttribute((const void*)align_scatter_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)((3 * 1024 + 1 + kChunkWaves * 1025 + kChunkWaves) * 4));
+                                       (int)align_lds_bytes(1024));
     if (err) return err;
     attr_set = true;
   }
@@ -201,6 +111,40 @@ int launch_align(const int32_t* ids, int M, int topk, int E, int bm,
                      ids, P, E, bm, nch, hist, sorted_ids, block_expert, offsets,
                      pair_pos, num_padded);
   return (int)hipGetLastError();
+}
+
+static size_t align_lds_bytes(int E) {
+  return (size_t)(3 * E + 2 + kChunkWaves * (E + 1) + kChunkWaves) * 4;
+}
+
+int launch_route_align(const float* logits, int M, int E, int k, int renorm, int bm,
+                       int32_t* ids, float* wts, int32_t* sorted_ids, int32_t* block_expert,
+                       int32_t* offsets, int32_t* pair_pos, int32_t* num_padded,
+                       hipStream_t stream) {
+  const size_t lds = (size_t)kChunk * 4 + align_lds_bytes(E);
+  const int nper = (E + kWave - 1) / kWave;
+#define RA_CASE(N)                                                                      \
+  if (nper <= N) {                                                                      \
+    static bool attr = false;                                                           \
+    if (!attr) {                                                                        \
+      int err = (int)hipFuncSetAttribute((const void*)route_align_kernel<N>,            \
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,    \
+                                         (int)(kChunk * 4 + align_lds_bytes(1024)));    \
+      if (err) return err;                                                              \
+      attr = true;                                                                      \
+    }                                                                                   \
+    hipLaunchKernelGGL(route_align_kernel<N>, dim3(1), dim3(kChunk), lds, stream, logits, \
+                       M, E, k, renorm, bm, ids, wts, sorted_ids, block_expert, offsets, \
+                       pair_pos, num_padded);                                           \
+    return (int)hipGetLastError();                                                      \
+  }
+  RA_CASE(1)
+  RA_CASE(2)
+  RA_CASE(4)
+  RA_CASE(8)
+  RA_CASE(16)
+#undef RA_CASE
+  return -1;
 }
 
 }  // namespace moe

@@ -673,6 +673,7 @@ static int g2s_dispatch(const GemmArgs& a, hipStream_t st) {
 }
 
 int launch_gemm2_stream(const GemmArgs& a, hipStream_t st) {
+  if (gemm2_ring_applies(a)) return launch_gemm2_ring(a, st);
   if (a.wt == DT_E4M3)
     return a.ot == DT_BF16 ? g2s_dispatch<DT_E4M3, DT_BF16>(a, st) : g2s_dispatch<DT_E4M3, DT_F32>(a, st);
   if (a.wt == DT_BF16)

@@ -20,6 +20,11 @@ int launch_align(const int32_t* ids, int M, int topk, int E, int bm,
                  int32_t* pair_pos, int32_t* num_padded, void* ws,
                  hipStream_t stream);
 
+int launch_route_align(const float* logits, int M, int E, int k, int renorm, int bm,
+                       int32_t* ids, float* wts, int32_t* sorted_ids, int32_t* block_expert,
+                       int32_t* offsets, int32_t* pair_pos, int32_t* num_padded,
+                       hipStream_t stream);
+
 int launch_quant_x(const void* x, int xt, size_t n, const float* static_scale,
                    float* partials, uint8_t* xq, float* sx, uint32_t* hmax_bits,
                    hipStream_t stream);
@@ -56,6 +61,8 @@ int launch_gemm1_stream(const GemmArgs& a, hipStream_t stream);
 bool gemm1_ring_applies(const GemmArgs& a);
 int launch_gemm1_ring(const GemmArgs& a, hipStream_t stream);
 int launch_gemm2_stream(const GemmArgs& a, hipStream_t stream);
+bool gemm2_ring_applies(const GemmArgs& a);
+int launch_gemm2_ring(const GemmArgs& a, hipStream_t stream);
 int launch_gemm1_tile(const GemmArgs& a, hipStream_t stream);
 int launch_gemm2_tile(const GemmArgs& a, hipStream_t stream);
 int launch_combine(const GemmArgs& a, hipStream_t stream);

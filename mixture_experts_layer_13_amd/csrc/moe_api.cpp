@@ -186,6 +186,38 @@ moe_status moe_align_permute(const int32_t* topk_ids, int32_t M, int32_t topk, i
   return hip_status(err, "align launch");
 }
 
+moe_status moe_route_align(const float* logits, int32_t M, int32_t E, int32_t topk,
+                           int32_t renormalize, int32_t block_m, int32_t* topk_ids,
+                           float* topk_weights, int32_t* sorted_pair_ids,
+                           int32_t* block_expert_ids, int32_t* expert_offsets,
+                           int32_t* pair_pos, int32_t* num_padded, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  moe_status s = check_route_dims(M, E, topk);
+  if (s) return s;
+  // one workgroup routes one token per wave: worth a launch only up to 16 rows
+  if ((long long)M * topk > 1024 || M > 16 || M == 0) {
+    s = moe_route_topk(logits, M, E, topk, renormalize, topk_ids, topk_weights, stream);
+    if (s) return s;
+    return moe_align_permute(topk_ids, M, topk, E, block_m, sorted_pair_ids, block_expert_ids,
+                             expert_offsets, pair_pos, num_padded, workspace, workspace_bytes,
+                             stream);
+  }
+  if (!valid_block_m(block_m))
+    return fail(MOE_ERR_SHAPE, "block_m=%d must be 16, 32, 64, 128 or 256", block_m);
+  if (!logits || !topk_ids || !topk_weights || !sorted_pair_ids || !block_expert_ids ||
+      !expert_offsets || !pair_pos || !num_padded)
+    return fail(MOE_ERR_NULL, "a required pointer is NULL");
+  for (const void* q : {(const void*)logits, (const void*)topk_ids, (const void*)topk_weights,
+                        (const void*)sorted_pair_ids, (const void*)block_expert_ids,
+                        (const void*)expert_offsets, (const void*)pair_pos,
+                        (const void*)num_padded})
+    if (!aligned(q, 4)) return fail(MOE_ERR_ALIGN, "route/align buffers must be 4-byte aligned");
+  int err = moe::launch_route_align(logits, M, E, topk, renormalize ? 1 : 0, block_m, topk_ids,
+                                    topk_weights, sorted_pair_ids, block_expert_ids,
+                                    expert_offsets, pair_pos, num_padded, (hipStream_t)stream);
+  return hip_status(err, "route_align launch");
+}
+
 moe_status moe_fused_forward(const moe_problem* p, const void* a, const void* w13,
                              const void* w2, const float* w13_scale, const float* w2_scale,
                              const float* a1_scale, const float* a2_scale,

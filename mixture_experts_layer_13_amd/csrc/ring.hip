@@ -25,6 +25,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace moe {
 
 constexpr int kRingD = 4;               // stages in the ring
@@ -49,6 +51,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
   asm volatile("" ::: "memory");
 }
+// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Workgroup barrier without the fence of __syncthreads (which would also wait
 // for the ring's outstanding loads); the empty asm keeps the compiler from
 // moving LDS accesses across it.
@@ -282,6 +293,349 @@ int launch_gemm1_ring(const GemmArgs& a, hipStream_t st) {
   if (a.wt == DT_E4M3)
     return ncb <= 1 ? g1r_launch<DT_E4M3, 1>(a, st) : g1r_launch<DT_E4M3, 2>(a, st);
   return ncb <= 1 ? g1r_launch<DT_BF16, 1>(a, st) : g1r_launch<DT_BF16, 2>(a, st);
+}
+
+}  // namespace moe
+
+// ===================================================== down GEMM (decode)
+//
+// Output-stationary down projection with the top-k combine fused, streaming
+// w2 through the same kind of ring.  Workgroup = 8 waves and 16 output rows
+// n0..n0+15; the stage sequence walks the active experts in id order, for
+// each expert its column passes (16*NCB tokens) and its K chunks (1 KiB of
+// each of the 16 rows = 8 K-steps, one per wave).  Each wave accumulates its
+// K-step's share for the current (expert, pass); on the pass's last chunk it
+// multiplies by scale * routing weight and adds into its own LDS accumulator
+// [M][16]; the 8 accumulators are summed in a fixed order at the end.  The
+// expert table and the per-position (token, weight) table are built in LDS
+// before the ring starts, so the steady loop issues no other memory reads
+// than the ring's and the h fragments travelling with it.
+namespace moe {
+
+constexpr int kG2RingWaves = 8;
+constexpr int kG2ChunkBytes = 1024;  // bytes of each w2 row per stage
+constexpr int kG2StageBytes = 16 * kPairStride;  // 2 halves x 8 two-row blocks
+constexpr int kG2RingMinM = 4;   // M range that takes the down-GEMM ring (measured:
+constexpr int kG2RingMaxM = 16;  // faster than the register kernel at T=8, slower at 1, 64)
+
+// (row r < 16, logical byte b < 1024) inside a down-GEMM stage
+__device__ __forceinline__ int ring2_off(int r, int b) {
+  return ((b >> 9) * 8 + (r >> 1)) * kPairStride + (r & 1) * kRingRowBytes +
+         ((b & 511) ^ ((r & 1) << 7));
+}
+
+struct G2Table {  // LDS tables of the down-GEMM ring
+  int* ek;        // [maxU] expert id
+  int* seg;       // [maxU] first sorted position
+  int* me;        // [maxU] real pairs
+  int* start;     // [maxU + 1] first stage of the expert
+  float* sc;      // [maxU] dequant scale of w2 (E4M3) times s_h, else 1
+  int* ptok;      // [cap] token of each sorted position (-1: padding)
+  float* pwt;     // [cap] routing weight of each sorted position
+};
+
+template <int WT, int OT, int NCB, int D>
+__global__ __launch_bounds__(512) void gemm2_ring_kernel(GemmArgs a, int maxU, int cap) {
+  constexpr int HT = (WT == DT_E4M3) ? DT_E4M3 : DT_BF16;
+  constexpr int NI = 2 + 2 * NCB;  // vector-memory instructions per issue
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int M = a.M, K = a.K, N = a.N;
+  const int n0 = blockIdx.x * 16;
+  constexpr int WB = Family<WT>::kBytes, HB = Family<HT>::kBytes;
+  const int nchunk = N * WB / kG2ChunkBytes;
+
+  // ---- LDS carve-up
+  char* ring = lds;
+  float* acc_lds = reinterpret_cast<float*>(lds + D * kG2StageBytes);  // [8][M][16]
+  int* ti = reinterpret_cast<int*>(acc_lds + kG2RingWaves * M * 16);
+  G2Table T;
+  T.ek = ti;
+  T.seg = T.ek + maxU;
+  T.me = T.seg + maxU;
+  T.start = T.me + maxU;
+  T.sc = reinterpret_cast<float*>(T.start + maxU + 1);
+  T.ptok = reinterpret_cast<int*>(T.sc + maxU);
+  T.pwt = reinterpret_cast<float*>(T.ptok + cap);
+  __shared__ int s_U;
+
+  // ---- tables: active experts (wave 0), per-position token/weight (all)
+  for (int i = tid; i < kG2RingWaves * M * 16; i += blockDim.x) acc_lds[i] = 0.0f;
+  const int npad = *a.num_padded;
+  for (int pos = tid; pos < npad; pos += blockDim.x) {
+    const int f = a.sorted_ids[pos];
+    const bool real = f < a.P;
+    T.ptok[pos] = real ? f / a.topk : -1;
+    T.pwt[pos] = real ? a.topk_w[f] : 0.0f;
+  }
+  if (wv == 0) {
+    int U = 0;
+    for (int base = 0; base < a.E; base += kWave) {
+      const int e = base + lane;
+      int o0 = 0, o1 = 0;
+      if (e < a.E) {
+        o0 = a.offsets[e];
+        o1 = a.offsets[e + 1];
+      }
+      const bool act = o1 > o0;
+      const uint64_t bal = __ballot(act);
+      if (act) {
+        const int k = U + __popcll(bal & lanemask_lt(lane));
+        T.ek[k] = e;
+        T.seg[k] = o0;
+        T.me[k] = o1 - o0;  // padded count; trimmed below
+      }
+      U += __popcll(bal);
+    }
+    if (lane == 0) s_U = U;
+  }
+  __syncthreads();
+  const int U = s_U;
+  // real count = padded count minus the trailing padding positions
+  for (int k = tid; k < U; k += blockDim.x) {
+    int m = T.me[k];
+    const int s0 = T.seg[k];
+    while (m > 0 && T.ptok[s0 + m - 1] < 0) --m;
+    T.me[k] = m;
+    float sc = 1.0f;
+    if (WT == DT_E4M3) sc = (*a.sh) * a.w2_scale[T.ek[k]];
+    T.sc[k] = sc;
+  }
+  __syncthreads();
+  if (wv == 0) {  // stage starts: prefix sum of npass * nchunk
+    int run = 0;
+    for (int base = 0; base < U; base += kWave) {
+      const int k = base + lane;
+      int v = 0;
+      if (k < U) v = ((T.me[k] + 16 * NCB - 1) / (16 * NCB)) * nchunk;
+      int x = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+      }
+      if (k < U) T.start[k] = run + x - v;
+      run += __shfl(x, 63, kWave);
+    }
+    if (lane == 0) T.start[U] = run;
+  }
+  __syncthreads();
+  const int S = T.start[U];
+
+  // ---- per-lane DMA geometry: wave wv issues blocks 2wv, 2wv+1
+  const int lrow = lane >> 5;
+  const int lb = ((lane & 31) << 4) ^ (lrow << 7);
+  int rowo[2], dst[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int bi = 2 * wv + q, rp = bi & 7;  // block bi: half bi >> 3, row pair rp
+    rowo[q] = n0 + 2 * rp + lrow;            // w2 row within the expert
+    dst[q] = bi * kPairStride;               // block order of ring2_off
+  }
+  const int hbyte[2] = {((2 * wv) >> 3) * 512 + lb, ((2 * wv + 1) >> 3) * 512 + lb};
+  const char* w2 = reinterpret_cast<const char*>(a.w2);
+  const char* hq = reinterpret_cast<const char*>(a.hq);
+
+  // cursor over stages: expert k, pass, chunk
+  struct Cur {
+    int k, pass, chunk;
+  };
+  auto advance = [&](Cur& c) {
+    if (++c.chunk == nchunk) {
+      c.chunk = 0;
+      ++c.pass;
+      if (T.start[c.k] + (c.pass) * nchunk >= T.start[c.k + 1]) {
+        c.pass = 0;
+        ++c.k;
+      }
+    }
+  };
+
+  Raw<HT> hs[D][NCB];
+  auto issue_dma = [&](const Cur& c, int slot) {
+    const int e = T.ek[c.k];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(w2 + ((size_t)e * K + rowo[q]) * N * WB +
+                                        (size_t)c.chunk * kG2ChunkBytes + hbyte[q]),
+          reinterpret_cast<void*>(ring + slot * kG2StageBytes + dst[q]), 16, 0, kRingAux);
+  };
+  auto h_src = [&](const Cur& c, int cb) {
+    const int col = c.pass * 16 * NCB + cb * 16 + r16;
+    const int pos = T.seg[c.k] + (col < T.me[c.k] ? col : 0);
+    return hq + (size_t)pos * N * HB + (size_t)c.chunk * kG2ChunkBytes * HB / WB +
+           (size_t)(wv * 128 + g * 32) * HB / WB;
+  };
+
+  f32x4 acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0, 0, 0, 0};
+  float* my = acc_lds + (size_t)wv * M * 16;
+
+  auto compute = [&](const Cur& c, int slot, const Raw<HT>* hx) {
+    const char* sb = ring + slot * kG2StageBytes;
+    const int o = ring2_off(r16, wv * 128 + g * 32);
+    Raw<WT> aw;
+    aw.q[0] = ld16(sb + o);
+    aw.q[1] = ld16(sb + o + 16);
+    const auto A = to_op<WT>(aw);
+    const int me = T.me[c.k];
+    const int ncb = min(NCB, (me - c.pass * 16 * NCB + 15) / 16);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      if (cb < ncb) acc[cb] = mma(A, to_op<HT>(hx[cb]), acc[cb]);
+    if (c.chunk == nchunk - 1) {  // end of this (expert, pass): flush
+      const float sc = T.sc[c.k];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int col = c.pass * 16 * NCB + cb * 16 + r16;
+        if (cb < ncb && col < me) {
+          const int pos = T.seg[c.k] + col;
+          const float m = sc * T.pwt[pos];
+          float* dd = my + (size_t)T.ptok[pos] * 16 + 4 * g;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dd[i] += acc[cb][i] * m;
+        }
+        acc[cb] = f32x4{0, 0, 0, 0};
+      }
+    }
+  };
+
+  Cur ci{0, 0, 0}, cc{0, 0, 0};
+  int issued = 0;
+  auto issue = [&](auto slot_c) {  // h fragments + DMA of stage `issued` into ring slot
+    constexpr int SLOT = decltype(slot_c)::value;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) hs[SLOT][cb] = load_raw<HT>(h_src(ci, cb));
+    issue_dma(ci, SLOT);
+    advance(ci);
+    ++issued;
+  };
+  if (S >= 2 * D - 1) {
+    static_for<0, D - 1>(issue);
+    int st = 0;
+    for (; st + 2 * D - 2 < S; st += D) {
+      static_for<0, D>([&](auto slot_c) {
+        constexpr int SLOT = decltype(slot_c)::value;
+        issue(std::integral_constant<int, (SLOT + D - 1) % D>{});
+        wait_vmcnt<(D - 1) * NI>();
+        wg_barrier();
+        compute(cc, SLOT, hs[SLOT]);
+        advance(cc);
+        wg_barrier();
+      });
+    }
+    // remaining stages: those already issued sit in the ring (their h
+    // fragments are re-read below), the rest is issued one at a time
+    for (; st < S; ++st) {
+      if (st >= issued) {
+        issue_dma(ci, st % D);
+        advance(ci);
+        ++issued;
+      }
+      wait_vmcnt<0>();
+      wg_barrier();
+      Raw<HT> hx[NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) hx[cb] = load_raw<HT>(h_src(cc, cb));
+      compute(cc, st % D, hx);
+      advance(cc);
+      wg_barrier();
+    }
+  } else {
+    for (int st = 0; st < S; ++st) {
+      issue_dma(ci, 0);
+      advance(ci);
+      Raw<HT> hx[NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) hx[cb] = load_raw<HT>(h_src(cc, cb));
+      wait_vmcnt<0>();
+      wg_barrier();
+      compute(cc, 0, hx);
+      advance(cc);
+      wg_barrier();
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < M * 4; i += blockDim.x) {
+    const int t = i >> 2, q = (i & 3) * 4;
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float s = 0.0f;
+      for (int w = 0; w < kG2RingWaves; ++w) s += acc_lds[((size_t)w * M + t) * 16 + q + j];
+      v[j] = s;
+    }
+    if (OT == DT_BF16) {
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + (size_t)t * K + n0 + q) =
+          make_uint2(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+                     f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
+    } else {
+      st16(reinterpret_cast<float*>(a.out) + (size_t)t * K + n0 + q,
+           i32x4{__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]),
+                 __float_as_int(v[3])});
+    }
+  }
+}
+
+constexpr int kG2RingDeep = 6;  // ring depth when the LDS allows it
+
+static size_t g2r_lds(const GemmArgs& a, int maxU, int cap, int D) {
+  return (size_t)D * kG2StageBytes + (size_t)kG2RingWaves * a.M * 16 * 4 +
+         ((size_t)maxU * 5 + 1) * 4 + (size_t)cap * 8;
+}
+
+static int g2r_depth(const GemmArgs& a) {
+  const int maxU = min(a.E, a.P);
+  const int cap = a.P + maxU * (a.block_m - 1);
+  const size_t budget = 160 * 1024 - 256;
+  if (g2r_lds(a, maxU, cap, kG2RingDeep) <= budget) return kG2RingDeep;
+  if (g2r_lds(a, maxU, cap, kRingD) <= budget) return kRingD;
+  return 0;
+}
+
+bool gemm2_ring_applies(const GemmArgs& a) {
+  if (!(a.wt == DT_BF16 || a.wt == DT_E4M3)) return false;
+  if (a.M < kG2RingMinM || a.M > kG2RingMaxM) return false;
+  const long long row = (long long)a.N * (a.wt == DT_BF16 ? 2 : 1);
+  if (row % kG2ChunkBytes) return false;
+  return g2r_depth(a) > 0;
+}
+
+template <int WT, int OT, int NCB, int D>
+static int g2r_launch(const GemmArgs& a, hipStream_t st) {
+  const int maxU = min(a.E, a.P);
+  const int cap = a.P + maxU * (a.block_m - 1);
+  const size_t lds = g2r_lds(a, maxU, cap, D);
+  static size_t attr = 0;  // largest dynamic LDS size enabled so far
+  if (lds > attr) {
+    int err = (int)hipFuncSetAttribute((const void*)gemm2_ring_kernel<WT, OT, NCB, D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err) return err;
+    attr = lds;
+  }
+  hipLaunchKernelGGL((gemm2_ring_kernel<WT, OT, NCB, D>), dim3(a.K / 16), dim3(512), lds, st, a,
+                     maxU, cap);
+  return (int)hipGetLastError();
+}
+
+template <int WT, int OT, int NCB>
+static int g2r_depth_dispatch(const GemmArgs& a, hipStream_t st) {
+  return g2r_depth(a) == kG2RingDeep ? g2r_launch<WT, OT, NCB, kG2RingDeep>(a, st)
+                                     : g2r_launch<WT, OT, NCB, kRingD>(a, st);
+}
+
+int launch_gemm2_ring(const GemmArgs& a, hipStream_t st) {
+  const int ncb = min((min(a.M, kStreamMaxM) + 15) / 16, kRingNcbMax);
+#define G2R(W, O)                                                                  \
+  return ncb <= 1 ? g2r_depth_dispatch<W, O, 1>(a, st) : g2r_depth_dispatch<W, O, 2>(a, st);
+  if (a.wt == DT_E4M3) {
+    if (a.ot == DT_BF16) G2R(DT_E4M3, DT_BF16) else G2R(DT_E4M3, DT_F32)
+  }
+  if (a.ot == DT_BF16) G2R(DT_BF16, DT_BF16) else G2R(DT_BF16, DT_F32)
+#undef G2R
 }
 
 }  // namespace moe

@@ -12,6 +12,7 @@
 // are computed in fp32 from exp(l - l_max), l_max being the first winner.
 #include "common.hpp"
 #include "launch.hpp"
+#include "route_align.hpp"
 
 namespace moe {
 
@@ -22,65 +23,12 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
-  const float* l = logits + (size_t)row * E;
-
-  float v[NPER];
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    int e = lane + kWave * i;
-    v[i] = (e < E) ? l[e] : 0.0f;
-  }
-  unsigned taken = 0;
-  float my_v = 0.0f;
-  int my_id = 0;
-  float lmax = 0.0f;
-
-  for (int j = 0; j < k; ++j) {
-    // lane-local best: ids increase with i, so a strict '>' keeps the lower id
-    float bv = 0.0f;
-    int bid = -1;
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-      int e = lane + kWave * i;
-      bool ok = (e < E) && !((taken >> i) & 1u);
-      if (ok && (bid < 0 || v[i] > bv)) {
-        bv = v[i];
-        bid = e;
-      }
-    }
-    // wave reduction on (value desc, id asc); bid < 0 marks "nothing left"
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      float ov = __shfl_xor(bv, o, kWave);
-      int oid = __shfl_xor(bid, o, kWave);
-      bool take = oid >= 0 && (bid < 0 || ov > bv || (ov == bv && oid < bid));
-      if (take) {
-        bv = ov;
-        bid = oid;
-      }
-    }
-    if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
-    if (j == 0) lmax = bv;
-    if (lane == j) {
-      my_v = bv;
-      my_id = bid;
-    }
-  }
-
-  float p = (lane < k) ? expf(my_v - lmax) : 0.0f;
-  float z;
-  if (renorm) {
-    z = wave_sum(p);
-  } else {
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NPER; ++i)
-      if (lane + kWave * i < E) s += expf(v[i] - lmax);
-    z = wave_sum(s);
-  }
+  int id;
+  float w;
+  route_row<NPER>(logits + (size_t)row * E, E, k, renorm, lane, id, w);
   if (lane < k) {
-    ids[(size_t)row * k + lane] = my_id;
-    wts[(size_t)row * k + lane] = p / z;
+    ids[(size_t)row * k + lane] = id;
+    wts[(size_t)row * k + lane] = w;
   }
 }
 

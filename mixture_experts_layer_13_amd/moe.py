@@ -19,7 +19,7 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_align_capacity", "moe_workspace_size",
            "moe_route_topk", "moe_align_permute", "moe_fused_forward", "moe_quantize_act",
-           "moe_set_profile_events")
+           "moe_set_profile_events", "moe_route_align")
 MOE_QUANT_WORKSPACE_BYTES = 8192
 
 
@@ -63,6 +63,9 @@ def lib():
         L.moe_quantize_act.restype = ctypes.c_int
         L.moe_set_profile_events.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         L.moe_set_profile_events.restype = None
+        L.moe_route_align.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, sz, vp]
+        L.moe_route_align.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -174,6 +177,24 @@ def moe_align_permute(topk_ids, E, block_m, workspace, alignment=None, stream=No
     return al
 
 
+def moe_route_align(logits, topk, renormalize, block_m, workspace, topk_ids=None,
+                    topk_weights=None, alignment=None, stream=None):
+    """Routing and alignment (one launch for M*topk <= 1024)."""
+    M, E = logits.shape
+    dev = logits.device
+    if topk_ids is None:
+        topk_ids = torch.empty(M, topk, dtype=torch.int32, device=dev)
+    if topk_weights is None:
+        topk_weights = torch.empty(M, topk, dtype=torch.float32, device=dev)
+    al = alignment or alloc_alignment(M, topk, E, block_m, dev)
+    _check(lib().moe_route_align(_ptr(logits), M, E, topk, int(bool(renormalize)), block_m,
+                                 _ptr(topk_ids), _ptr(topk_weights), _ptr(al.sorted_pair_ids),
+                                 _ptr(al.block_expert_ids), _ptr(al.expert_offsets),
+                                 _ptr(al.pair_pos), _ptr(al.num_padded), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    return topk_ids, topk_weights, al
+
+
 def moe_fused_forward(problem, x, w13, w2, topk_weights, alignment, out, workspace,
                       w13_scale=None, w2_scale=None, a1_scale=None, a2_scale=None,
                       stream=None):
@@ -210,10 +231,8 @@ class FusedMoE:
         self.out = torch.empty(M, K, dtype=out_dtype, device=device)
 
     def __call__(self, x, logits, stream=None):
-        moe_route_topk(logits, self.topk, self.renormalize, self.topk_ids, self.topk_weights,
-                       stream)
-        moe_align_permute(self.topk_ids, self.E, self.block_m, self.workspace, self.alignment,
-                          stream)
+        moe_route_align(logits, self.topk, self.renormalize, self.block_m, self.workspace,
+                        self.topk_ids, self.topk_weights, self.alignment, stream)
         moe_fused_forward(self.problem, x, self.w13, self.w2, self.topk_weights, self.alignment,
                           self.out, self.workspace, self.w13_scale, self.w2_scale,
                           self.a1_scale, self.a2_scale, stream)

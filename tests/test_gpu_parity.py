@@ -117,6 +117,28 @@ def test_align_is_deterministic():
     assert torch.equal(s1[:n], b.sorted_pair_ids[:n])
 
 
+@pytest.mark.parametrize("T,E,k,bm", [(1, 64, 8, 16), (64, 64, 8, 16), (16, 8, 2, 32), (37, 1000, 17, 64),
+                                       (128, 256, 8, 16), (129, 64, 8, 128), (3, 2, 1, 16)])
+def test_route_align_fused_equals_separate_calls(T, E, k, bm):
+    logits = inputs.make_logits(T, E, 31 + T, 1.1 if E > 8 else 0.0, device=DEV)
+    p = moe.make_problem(max(T, 1), 128, 128, E, k, bm, torch.bfloat16, torch.bfloat16, torch.bfloat16)
+    ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device=DEV)
+    ids_a, w_a = moe.moe_route_topk(logits, k, True)
+    al_a = moe.moe_align_permute(ids_a, E, bm, ws)
+    torch.cuda.synchronize()
+    ids_b, w_b, al_b = moe.moe_route_align(logits, k, True, bm, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ids_a, ids_b) and torch.equal(w_a, w_b)
+    n = int(al_a.num_padded.item())
+    assert n == int(al_b.num_padded.item())
+    assert torch.equal(al_a.expert_offsets, al_b.expert_offsets)
+    assert torch.equal(al_a.sorted_pair_ids[:n], al_b.sorted_pair_ids[:n])
+    assert torch.equal(al_a.block_expert_ids[: n // bm], al_b.block_expert_ids[: n // bm])
+    assert torch.equal(al_a.pair_pos[: T * k], al_b.pair_pos[: T * k])
+    ref = oracle.align(oracle.route_topk(logits.cpu().numpy(), k, True)[0], E, bm)
+    assert np.array_equal(al_b.sorted_pair_ids[:n].cpu().numpy(), ref["sorted_pair_ids"])
+
+
 # ------------------------------------------------------- activation quant
 
 @pytest.mark.parametrize("shape,dtype", [((1, 4096), torch.bfloat16), ((64, 4096), torch.bfloat16),
