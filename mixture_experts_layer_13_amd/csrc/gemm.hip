@@ -701,6 +701,7 @@ static int g1t_dispatch(const GemmArgs& a, hipStream_t st) {
 }
 
 int launch_gemm1_tile(const GemmArgs& a, hipStream_t st) {
+  if (pf_applies(a, true)) return launch_gemm1_prefill(a, st);
   // tile operands: bf16 family needs bf16 activations (f32 ones are cast first)
   if (a.wt == DT_E4M3) return g1t_dispatch<DT_E4M3, DT_E4M3>(a, st);
   if (a.wt == DT_BF16) return g1t_dispatch<DT_BF16, DT_BF16>(a, st);
@@ -724,6 +725,7 @@ static int g2t_dispatch(const GemmArgs& a, hipStream_t st) {
 }
 
 int launch_gemm2_tile(const GemmArgs& a, hipStream_t st) {
+  if (pf_applies(a, false)) return launch_gemm2_prefill(a, st);
   if (a.wt == DT_E4M3) return g2t_dispatch<DT_E4M3>(a, st);
   if (a.wt == DT_BF16) return g2t_dispatch<DT_BF16>(a, st);
   return g2t_dispatch<DT_F32>(a, st);
