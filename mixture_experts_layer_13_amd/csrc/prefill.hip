@@ -71,6 +71,54 @@ __device__ __forceinline__ void pf_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// MFMA instructions per chunk and wave.
+template <int T>
+constexpr int kPfMfma() {
+  return kPfTA * kPfTB * (T == DT_E4M3 ? 1 : 2);
+}
+constexpr int kPfDs = 2 * (kPfTA + kPfTB);  // fragment reads per chunk and wave
+
+// Scheduling of one chunk's instruction stream: the kPfNI DMA instructions of
+// chunk c + 3 and the kPfDs fragment reads of chunk c + 1 are spread over the
+// first three quarters of chunk c's MFMAs (a few MFMAs, one read, one DMA
+// instruction, ...), so that they issue in the MFMAs' shadow and the reads
+// have completed by the next barrier.  sched_group_barrier masks: 0x008 MFMA,
+// 0x100 DS read, 0x020 VMEM read.
+template <int NMF, int I = 0>
+__device__ __forceinline__ void pf_interleave() {
+  constexpr int per = (NMF * 3 / 4) / kPfDs;  // MFMAs before each read
+  if constexpr (I < kPfDs) {
+    __builtin_amdgcn_sched_group_barrier(0x008, per, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if constexpr (I < kPfNI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    pf_interleave<NMF, I + 1>();
+  } else {
+    __builtin_amdgcn_sched_group_barrier(0x008, NMF - per * kPfDs, 0);
+  }
+}
+
+// Scheduling of one bf16 half chunk: its NMF MFMAs with the kPfDs / 2
+// fragment reads of the next half spread over the first three quarters, and
+// (second half) the kPfNI DMA instructions of the refill as well.
+template <int NMF, bool DMA, int I = 0>
+__device__ __forceinline__ void pf_interleave_half() {
+  constexpr int nds = kPfDs / 2;
+  constexpr int per = (NMF * 3 / 4) / nds;
+  if constexpr (I < nds) {
+    __builtin_amdgcn_sched_group_barrier(0x008, per, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if constexpr (DMA && I < kPfNI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    pf_interleave_half<NMF, DMA, I + 1>();
+  } else {
+    __builtin_amdgcn_sched_group_barrier(0x008, NMF - per * nds, 0);
+  }
+}
+
+// Raw buffer resource over [base, base + bytes) (gfx9 word 3: 32-bit data).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // XCD-aware task order: the hardware deals consecutive workgroup ids
 // round-robin over the 8 XCDs; each XCD is given a contiguous range of
 // (weight tile, token block) tasks, token block fastest, so that the blocks
@@ -92,70 +140,94 @@ __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   int nt, mb;
   pf_task(nt, mb);
-  if (mb * kPfTok >= *a.num_padded) return;  // uniform: past the last block
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int r16 = lane & 15, g = lane >> 4;
   const int wr = wv >> 1, wc = wv & 1;
-  const int e = a.block_expert[(mb * kPfTok) / a.block_m];
   const int Kd = G1 ? a.K : a.N;  // contraction length
   constexpr int EB = Family<T>::kBytes;
-  const size_t rowb = (size_t)Kd * EB;
+  const uint32_t rowb = (uint32_t)Kd * EB;
   const int nchunks = (int)(rowb / kPfChunk);
-
-  // Per-lane DMA sources of chunk 0.  A wave's 8 weight instructions cover
-  // 64 consecutive tile rows, which are 64 consecutive rows of the weight
-  // matrix (gate or up block for the gate/up product); the rotation of row r
-  // only depends on r mod 8, so one lane offset serves all of them.
   const int lrow = lane >> 3, pcol = lane & 7;
-  const char* wbase;
+
+  // Metadata, all loads in flight together (every index below is inside the
+  // arrays for any block below max_blocks, valid or not).
+  const int npad = *a.num_padded;
+  const int e = a.block_expert[(mb * kPfTok) / a.block_m];
+  int fx[kPfXInstr];  // pair index of the token rows this lane's DMA gathers
+#pragma unroll
+  for (int q = 0; q < kPfXInstr; ++q) fx[q] = a.sorted_ids[mb * kPfTok + 8 * (wv * kPfXInstr + q) + lrow];
+  int fe[kPfTB];  // pair index of the token columns this lane's results belong to
+#pragma unroll
+  for (int j = 0; j < kPfTB; ++j) fe[j] = a.sorted_ids[mb * kPfTok + 64 * wc + 16 * j + r16];
+  if (mb * kPfTok >= npad) return;  // uniform: past the last block
+
+  // DMA sources.  A wave's 8 weight instructions cover 64 consecutive tile
+  // rows = 64 consecutive rows of one weight matrix (the gate or up block for
+  // the gate/up product); the rotation only depends on the row mod 8, so one
+  // lane offset serves all of them and the instruction / chunk offsets are
+  // scalar.
+  __amdgpu_buffer_rsrc_t wres, xres;
+  uint32_t w_sbase, x_sbase = 0;
+  const uint32_t w_voff = lrow * rowb + pf_logical(lrow, pcol) * 16;
+  uint32_t x_voff[kPfXInstr];
   {
     const int r0 = 64 * wv;  // first tile row of this wave's weight DMA
-    size_t grow0;
     if (G1) {
       const int h0 = nt * 128 + 64 * (r0 >> 7);  // first intermediate column
-      grow0 = (size_t)e * 2 * a.N + ((r0 & 127) < 64 ? h0 : a.N + h0);
-      wbase = reinterpret_cast<const char*>(a.w13) + grow0 * rowb;
-    } else {
-      grow0 = (size_t)e * a.K + nt * kPfRows + r0;
-      wbase = reinterpret_cast<const char*>(a.w2) + grow0 * rowb;
-    }
-  }
-  const uint32_t woff = (uint32_t)(lrow * rowb) + (uint32_t)(pf_logical(lrow, pcol) * 16);
-  const char* xsrc[kPfXInstr];
+      wres = pf_rsrc(reinterpret_cast<const char*>(a.w13) + (size_t)e * 2 * a.N * rowb, 2 * a.N * rowb);
+      w_sbase = (uint32_t)((r0 & 127) < 64 ? h0 : a.N + h0) * rowb;
+      xres = pf_rsrc(a.x, (uint32_t)a.M * rowb);
 #pragma unroll
-  for (int q = 0; q < kPfXInstr; ++q) {
-    const int r = 8 * (wv * kPfXInstr + q) + lrow;  // token row 0..127
-    const int c = pf_logical(r, pcol);
-    const int pos = mb * kPfTok + r;
-    if (G1) {
-      int f = a.sorted_ids[pos];
-      if (f >= a.P) f = 0;  // padding row: any valid row, never stored
-      xsrc[q] = reinterpret_cast<const char*>(a.x) + (size_t)(f / a.topk) * rowb + c * 16;
+      for (int q = 0; q < kPfXInstr; ++q) {
+        const int r = 8 * (wv * kPfXInstr + q) + lrow;
+        const int f = fx[q] < a.P ? fx[q] : 0;  // padding row: any valid row, never stored
+        x_voff[q] = (uint32_t)(f / a.topk) * rowb + pf_logical(r, pcol) * 16;
+      }
     } else {
-      xsrc[q] = reinterpret_cast<const char*>(a.hq) + (size_t)pos * rowb + c * 16;
+      wres = pf_rsrc(reinterpret_cast<const char*>(a.w2) + (size_t)e * a.K * rowb, a.K * rowb);
+      w_sbase = (uint32_t)(nt * kPfRows + r0) * rowb;
+      xres = pf_rsrc(reinterpret_cast<const char*>(a.hq) + (size_t)mb * kPfTok * rowb, kPfTok * rowb);
+      x_sbase = (uint32_t)(32 * wv) * rowb;
+#pragma unroll
+      for (int q = 0; q < kPfXInstr; ++q) x_voff[q] = lrow * rowb + pf_logical(lrow, pcol) * 16;
     }
   }
+  const __amdgpu_buffer_rsrc_t null_res = pf_rsrc(a.x, 0);  // every access out of range
 
+  // DMA of `chunk` into stage `slot`; past the last chunk the instructions
+  // still issue (the instruction stream of every chunk is the same) through a
+  // resource of size 0, which fetches nothing.
   auto issue = [&](int chunk, int slot) {
+    const bool real = chunk < nchunks;
+    const __amdgpu_buffer_rsrc_t wr_ = real ? wres : null_res;
+    const __amdgpu_buffer_rsrc_t xr_ = real ? xres : null_res;
     char* sb = lds + slot * kPfStageBytes;
-    const size_t off = (size_t)chunk * kPfChunk;
+    const uint32_t off = (uint32_t)chunk * kPfChunk;
 #pragma unroll
     for (int q = 0; q < kPfWInstr; ++q)
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(wbase + off + (size_t)(8 * q) * rowb + woff),
-          reinterpret_cast<void*>(sb + (wv * kPfWInstr + q) * 1024), 16, 0, kPfAux);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wr_, (__attribute__((address_space(3))) void*)(sb + (wv * kPfWInstr + q) * 1024), 16, w_voff,
+          w_sbase + (uint32_t)(8 * q) * rowb + off, 0, kPfAux);
 #pragma unroll
     for (int q = 0; q < kPfXInstr; ++q)
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(xsrc[q] + off),
-          reinterpret_cast<void*>(sb + kPfWBytes + (wv * kPfXInstr + q) * 1024), 16, 0, kPfAux);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xr_, (__attribute__((address_space(3))) void*)(sb + kPfWBytes + (wv * kPfXInstr + q) * 1024),
+          16, x_voff[q], x_sbase + (uint32_t)(8 * q) * (G1 ? 0u : rowb) + off, 0, kPfAux);
   };
 
+  // The empty asm makes each zero accumulator an opaque value of its own:
+  // otherwise the compiler shares one zero register among all of them in the
+  // first iteration and then shuffles accumulators between registers inside
+  // the loop.
   f32x4 acc[kPfTA][kPfTB];
 #pragma unroll
   for (int i = 0; i < kPfTA; ++i)
 #pragma unroll
-    for (int j = 0; j < kPfTB; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+    for (int j = 0; j < kPfTB; ++j) {
+      acc[i][j] = f32x4{0, 0, 0, 0};
+      asm volatile("" : "+a"(acc[i][j]));
+    }
 
   // LDS offsets of this lane's fragments (logical columns g and g + 4); tile
   // i adds i * 16 rows = i * 2048 bytes (the rotation repeats every 8 rows)
@@ -166,67 +238,98 @@ __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a) {
     boff[h] = kPfWBytes + pf_off(64 * wc + r16, g + 4 * h);
   }
 
-  // Fragments of chunk c are read from LDS right after the barrier that
-  // publishes it and consumed one iteration later, so the MFMAs of chunk c - 1
-  // cover the LDS latency of chunk c; the DMA runs two chunks ahead.
-  auto load_frags = [&](int slot, Raw<T> (&A)[kPfTA], Raw<T> (&B)[kPfTB]) {
-    const char* sb = lds + slot * kPfStageBytes;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int j = 0; j < kPfTB; ++j) B[j].q[h] = ld16(sb + boff[h] + j * 16 * kPfChunk);
-#pragma unroll
-      for (int i = 0; i < kPfTA; ++i) A[i].q[h] = ld16(sb + aoff[h] + i * 16 * kPfChunk);
-    }
-  };
-  auto compute = [&](const Raw<T> (&A)[kPfTA], const Raw<T> (&B)[kPfTB]) {
-#pragma unroll
-    for (int i = 0; i < kPfTA; ++i) {
-      auto Ai = to_op<T>(A[i]);
-#pragma unroll
-      for (int j = 0; j < kPfTB; ++j) acc[i][j] = mma(Ai, to_op<T>(B[j]), acc[i][j]);
-    }
-  };
-  // Iteration c (c + 1 < nchunks): wait for chunk c + 1, barrier (chunk c + 1
-  // visible; every wave holds chunk c's fragments, so stage c % 3 is free),
-  // refill that stage with chunk c + 3, read chunk c + 1's fragments, multiply
-  // chunk c.  The accumulators flow through straight-line code only (no
-  // branch around an MFMA), so they keep their registers across iterations.
-  auto step = [&](int c, Raw<T> (&Ac)[kPfTA], Raw<T> (&Bc)[kPfTB], Raw<T> (&An)[kPfTA],
-                  Raw<T> (&Bn)[kPfTB]) {
-    if (c + 2 < nchunks)
-      pf_wait_vmcnt<kPfNI>();
-    else
-      pf_wait_vmcnt<0>();
-    pf_barrier();
-    if (c + 3 < nchunks) issue(c + 3, c % 3);
-    load_frags((c + 1) % 3, An, Bn);
-    compute(Ac, Bc);
-  };
-
   issue(0, 0);
-  if (nchunks > 1) issue(1, 1);
-  if (nchunks > 2) issue(2, 2);
-  if (nchunks > 2)
-    pf_wait_vmcnt<2 * kPfNI>();
-  else if (nchunks > 1)
-    pf_wait_vmcnt<kPfNI>();
-  else
-    pf_wait_vmcnt<0>();
+  issue(1, 1);
+  issue(2, 2);
+  pf_wait_vmcnt<2 * kPfNI>();
   pf_barrier();
-  Raw<T> A0[kPfTA], B0[kPfTB], A1[kPfTA], B1[kPfTB];
-  load_frags(0, A0, B0);
-  int c = 0;
-  for (; c + 2 < nchunks; c += 2) {
-    step(c, A0, B0, A1, B1);
-    step(c + 1, A1, B1, A0, B0);
+
+  if constexpr (T == DT_BF16) {
+    // bf16: a chunk is two K halves of 32 (16-byte columns g and g + 4 of
+    // each row); half 0 of chunk c is in registers when iteration c starts.
+    //   multiply half 0 while reading half 1 of chunk c;
+    //   wait for chunk c + 1, barrier (every wave holds all of chunk c, so
+    //   stage c % 3 is free), refill it with chunk c + 3;
+    //   multiply half 1 while reading half 0 of chunk c + 1.
+    // Each register set keeps one role, so the loop body is straight-line
+    // code; the last iteration reads a stale stage and the DMA past the end
+    // fetches nothing, so every iteration is the same.
+    i32x4 A0[kPfTA], B0[kPfTB], A1[kPfTA], B1[kPfTB];
+    auto load_half = [&](int h, int slot, i32x4 (&A)[kPfTA], i32x4 (&B)[kPfTB]) {
+      const char* sb = lds + slot * kPfStageBytes;
+#pragma unroll
+      for (int j = 0; j < kPfTB; ++j) B[j] = ld16(sb + boff[h] + j * 16 * kPfChunk);
+#pragma unroll
+      for (int i = 0; i < kPfTA; ++i) A[i] = ld16(sb + aoff[h] + i * 16 * kPfChunk);
+    };
+    auto mult_half = [&](const i32x4 (&A)[kPfTA], const i32x4 (&B)[kPfTB]) {
+#pragma unroll
+      for (int i = 0; i < kPfTA; ++i)
+#pragma unroll
+        for (int j = 0; j < kPfTB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(A[i]), as_bf16x8(B[j]), acc[i][j],
+                                                              0, 0, 0);
+    };
+    load_half(0, 0, A0, B0);
+    for (int c = 0; c < nchunks; ++c) {
+      const int slot = c % 3;
+      load_half(1, slot, A1, B1);
+      mult_half(A0, B0);
+      pf_interleave_half<kPfTA * kPfTB, false>();
+      pf_wait_vmcnt<kPfNI>();
+      pf_barrier();
+      issue(c + 3, slot);
+      load_half(0, slot == 2 ? 0 : slot + 1, A0, B0);
+      mult_half(A1, B1);
+      pf_interleave_half<kPfTA * kPfTB, true>();
+    }
+  } else {
+    // E4M3: one MFMA takes a whole 128-byte chunk, so whole chunks are
+    // double-buffered: fragments of chunk c are read right after the barrier
+    // that publishes it and multiplied one iteration later.
+    Raw<T> A0[kPfTA], B0[kPfTB], A1[kPfTA], B1[kPfTB];
+    auto load_frags = [&](int slot, Raw<T> (&A)[kPfTA], Raw<T> (&B)[kPfTB]) {
+      const char* sb = lds + slot * kPfStageBytes;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int j = 0; j < kPfTB; ++j) B[j].q[h] = ld16(sb + boff[h] + j * 16 * kPfChunk);
+#pragma unroll
+        for (int i = 0; i < kPfTA; ++i) A[i].q[h] = ld16(sb + aoff[h] + i * 16 * kPfChunk);
+      }
+    };
+    auto compute = [&](const Raw<T> (&A)[kPfTA], const Raw<T> (&B)[kPfTB]) {
+#pragma unroll
+      for (int i = 0; i < kPfTA; ++i)
+#pragma unroll
+        for (int j = 0; j < kPfTB; ++j) acc[i][j] = mma(to_op<T>(A[i]), to_op<T>(B[j]), acc[i][j]);
+    };
+    // Iteration c: wait for chunk c + 1, barrier (chunk c + 1 visible; every
+    // wave holds chunk c's fragments, so stage c % 3 is free), refill that
+    // stage with chunk c + 3, read chunk c + 1's fragments, multiply chunk c.
+    auto step = [&](int c, Raw<T> (&Ac)[kPfTA], Raw<T> (&Bc)[kPfTB], Raw<T> (&An)[kPfTA],
+                    Raw<T> (&Bn)[kPfTB]) {
+      pf_wait_vmcnt<kPfNI>();
+      pf_barrier();
+      issue(c + 3, c % 3);
+      load_frags((c + 1) % 3, An, Bn);
+      compute(Ac, Bc);
+      pf_interleave<kPfMfma<T>()>();
+    };
+    load_frags(0, A0, B0);
+    int c = 0;
+    for (; c + 2 < nchunks; c += 2) {
+      step(c, A0, B0, A1, B1);
+      step(c + 1, A1, B1, A0, B0);
+    }
+    if (c + 1 < nchunks) {  // two chunks left
+      step(c, A0, B0, A1, B1);
+      compute(A1, B1);
+    } else {  // one chunk left
+      compute(A0, B0);
+    }
   }
-  if (c + 1 < nchunks) {  // two chunks left
-    step(c, A0, B0, A1, B1);
-    compute(A1, B1);
-  } else {  // one chunk left
-    compute(A0, B0);
-  }
+  pf_wait_vmcnt<0>();  // no DMA may land after the workgroup's LDS is released
 
   if constexpr (G1) {
     float scale = 1.0f;
@@ -235,7 +338,7 @@ __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < kPfTB; ++j) {
       const int pos = mb * kPfTok + 64 * wc + 16 * j + r16;
-      if (a.sorted_ids[pos] < a.P) {
+      if (fe[j] < a.P) {
 #pragma unroll
         for (int i = 0; i < kPfTA / 2; ++i) {
           float h[4];
@@ -267,7 +370,7 @@ __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < kPfTB; ++j) {
       const int pos = mb * kPfTok + 64 * wc + 16 * j + r16;
-      const int f = a.sorted_ids[pos];
+      const int f = fe[j];
       if (f < a.P) {
         const float m = scale * a.topk_w[f];
 #pragma unroll
@@ -288,6 +391,10 @@ bool pf_applies(const GemmArgs& a, bool gemm1) {
   const bool types = (a.wt == DT_BF16 && (gemm1 ? a.xt == DT_BF16 : true)) ||
                      (a.wt == DT_E4M3 && (gemm1 ? a.xt == DT_E4M3 : true));
   if (!types || a.block_m < kPfTok) return false;
+  // buffer resources take 32-bit byte ranges
+  const size_t wb = (a.wt == DT_E4M3) ? 1 : 2;
+  const size_t lim = (size_t)1 << 31;
+  if ((size_t)2 * a.N * a.K * wb >= lim || (size_t)a.M * a.K * wb >= lim) return false;
   return gemm1 ? (a.N % 128 == 0) : (a.K % kPfRows == 0);
 }
 
