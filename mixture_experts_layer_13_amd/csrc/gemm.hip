@@ -554,7 +554,8 @@ __global__ __launch_bounds__(256) void gemm1_tile_kernel(GemmArgs a) {
   }
 }
 
-// Down projection of one token block: y[pos] = routing weight * scale * (W2 h).
+// Down projection of one token block: y[pos] = scale * (W2 h); the routing
+// weight is applied by the combine.
 template <int WT, int BM>
 __global__ __launch_bounds__(256) void gemm2_tile_kernel(GemmArgs a) {
   constexpr int HT = (WT == DT_E4M3) ? DT_E4M3 : DT_BF16;
@@ -597,35 +598,57 @@ __global__ __launch_bounds__(256) void gemm2_tile_kernel(GemmArgs a) {
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const int pos = mb * BM + cb * 16 + r16;
-    const int f = a.sorted_ids[pos];
-    if (f < a.P) {
-      const float m = scale * a.topk_w[f];
+    if (a.sorted_ids[pos] < a.P) {
 #pragma unroll
       for (int na = 0; na < 2; ++na) {
-        float* dst = a.y + (size_t)pos * K + n0 + na * 16 + 4 * g;
-        st16(dst, i32x4{__float_as_int(acc[na][cb][0] * m), __float_as_int(acc[na][cb][1] * m),
-                        __float_as_int(acc[na][cb][2] * m), __float_as_int(acc[na][cb][3] * m)});
+        const size_t idx = (size_t)pos * K + n0 + na * 16 + 4 * g;
+        const float v[4] = {acc[na][cb][0] * scale, acc[na][cb][1] * scale, acc[na][cb][2] * scale,
+                            acc[na][cb][3] * scale};
+        if (a.ot == DT_BF16)
+          store_out4<DT_BF16>(a.y, idx, v);
+        else
+          store_out4<DT_F32>(a.y, idx, v);
       }
     }
   }
 }
 
-// out[t] = sum over slots j (in routing order) of y[pair_pos[t*k + j]].
+// out[t] = sum over slots j (in routing order) of w[t, j] * y[pair_pos[t*k + j]]
+// (y in the output's type: bf16 or fp32; the sum in fp32).  Workgroup = one
+// token row (blockIdx.x) x 2048 columns (blockIdx.y), 8 columns per thread;
+// the slot positions and weights are wave-uniform.
 template <int OT>
 __global__ __launch_bounds__(256) void combine_kernel(GemmArgs a) {
   const int K = a.K;
-  const size_t i4 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i4 >= (size_t)a.M * K) return;
-  const int t = (int)(i4 / K), n = (int)(i4 % K);
-  float v[4] = {0, 0, 0, 0};
+  const int t = blockIdx.x;
+  const int n = (blockIdx.y * 256 + threadIdx.x) * 8;
+  if (n >= K) return;
+  float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int j = 0; j < a.topk; ++j) {
     const int pos = a.pair_pos[(size_t)t * a.topk + j];
     if (pos < 0) continue;
-    i32x4 q = ld16(a.y + (size_t)pos * K + n);
+    const float w = a.topk_w[(size_t)t * a.topk + j];
+    const size_t at = (size_t)pos * K + n;
+    if (OT == DT_BF16) {
+      const i32x4 q = ld16(reinterpret_cast<const uint16_t*>(a.y) + at);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) v[c] += __int_as_float(q[c]);
+      for (int c = 0; c < 4; ++c) {
+        v[2 * c] += w * bf16_bits_to_f32((uint32_t)q[c] & 0xffffu);
+        v[2 * c + 1] += w * bf16_bits_to_f32((uint32_t)q[c] >> 16);
+      }
+    } else {
+      const i32x4 q0 = ld16(reinterpret_cast<const float*>(a.y) + at);
+      const i32x4 q1 = ld16(reinterpret_cast<const float*>(a.y) + at + 4);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        v[c] += w * __int_as_float(q0[c]);
+        v[4 + c] += w * __int_as_float(q1[c]);
+      }
+    }
   }
-  store_out4<OT>(a.out, i4, v);
+  const size_t o = (size_t)t * K + n;
+  store_out4<OT>(a.out, o, v);
+  store_out4<OT>(a.out, o + 4, v + 4);
 }
 
 __global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict__ src,
@@ -732,8 +755,7 @@ int launch_gemm2_tile(const GemmArgs& a, hipStream_t st) {
 }
 
 int launch_combine(const GemmArgs& a, hipStream_t st) {
-  size_t n4 = (size_t)a.M * a.K / 4;
-  dim3 grid((unsigned)((n4 + 255) / 256));
+  dim3 grid((unsigned)a.M, (unsigned)((a.K + 2047) / 2048));
   if (a.ot == DT_BF16)
     hipLaunchKernelGGL(combine_kernel<DT_BF16>, grid, dim3(256), 0, st, a);
   else

@@ -53,7 +53,8 @@ struct GemmArgs {
   void* h;               // [cap, N] bf16 (bf16 family) or fp32 (E4M3)
   const void* hq;        // GEMM2 operand: h itself (bf16) or its E4M3 codes
   uint32_t* hmax_bits;   // E4M3: running max |h|
-  float* y;              // tile path: [cap, K] fp32 weighted expert outputs
+  void* y;               // tile path: [cap, K] expert outputs before the routing
+                         // weight, bf16 when the layer output is bf16, else fp32
   void* out;             // [M, K]
 };
 

@@ -289,7 +289,7 @@ moe_status moe_fused_forward(const moe_problem* p, const void* a, const void* w1
   g.pair_pos = pair_pos;
   g.num_padded = num_padded;
   g.h = ws + L.h;
-  g.y = (float*)(ws + L.y);
+  g.y = ws + L.y;
   g.out = out;
 
   int err = 0;

@@ -134,7 +134,7 @@ __device__ __forceinline__ void pf_task(int& nt, int& mb) {
 }
 
 // G1 = true: gate/up product + SiLU * up -> h.  G1 = false: down product
-// times the routing weight -> y (one row per sorted position).
+// -> y (one row per sorted position, routing weight not yet applied).
 template <int T, bool G1>
 __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -365,19 +365,27 @@ __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a) {
       if (lane == 0 && hmax > 0.0f) atomicMax(a.hmax_bits, __float_as_uint(hmax));
     }
   } else {
+    // y rows hold W2 h of each pair; the routing weight is applied where the
+    // top-k rows of a token are summed.
     float scale = 1.0f;
     if (T == DT_E4M3) scale = (*a.sh) * a.w2_scale[e];
+    const bool ybf = a.ot == DT_BF16;
 #pragma unroll
     for (int j = 0; j < kPfTB; ++j) {
       const int pos = mb * kPfTok + 64 * wc + 16 * j + r16;
-      const int f = fe[j];
-      if (f < a.P) {
-        const float m = scale * a.topk_w[f];
+      if (fe[j] < a.P) {
 #pragma unroll
         for (int i = 0; i < kPfTA; ++i) {
-          float* dst = a.y + (size_t)pos * a.K + nt * kPfRows + 128 * wr + 16 * i + 4 * g;
-          st16(dst, i32x4{__float_as_int(acc[i][j][0] * m), __float_as_int(acc[i][j][1] * m),
-                          __float_as_int(acc[i][j][2] * m), __float_as_int(acc[i][j][3] * m)});
+          const size_t idx = (size_t)pos * a.K + nt * kPfRows + 128 * wr + 16 * i + 4 * g;
+          const float v[4] = {acc[i][j][0] * scale, acc[i][j][1] * scale, acc[i][j][2] * scale,
+                              acc[i][j][3] * scale};
+          if (ybf)
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + idx) =
+                make_uint2(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+                           f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
+          else
+            st16(reinterpret_cast<float*>(a.y) + idx,
+                 i32x4{__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3])});
         }
       }
     }
