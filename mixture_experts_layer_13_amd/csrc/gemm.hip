@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(GemmArgs a) {
     // wave wv finishes column blocks cb = wv, wv + 4, ...
     for (int cb = wv; cb < ncb; cb += kG1Waves) {
       const int col = c0 + cb * 16 + r16;
-      float h[4];
+      float h[4], g4[4], u4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float gs = 0.0f, us = 0.0f;
@@ -199,9 +199,13 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(GemmArgs a) {
           gs += red[w][0][cb][i][lane];
           us += red[w][1][cb][i][lane];
         }
-        h[i] = silu(gs * scale) * (us * scale);
+        g4[i] = gs * scale;
+        u4[i] = us * scale;
+        h[i] = silu(g4[i]) * u4[i];
       }
-      if (col < me) {
+      if (a.probe) {
+        if (col < me) probe_store(a, (size_t)(seg0 + col), n0 + 4 * g, g4, u4);
+      } else if (col < me) {
         const size_t idx = (size_t)(seg0 + col) * N + n0 + 4 * g;
         if (WT == DT_E4M3) {
           st16(reinterpret_cast<float*>(a.h) + idx,
@@ -531,11 +535,17 @@ __global__ __launch_bounds__(256) void gemm1_tile_kernel(GemmArgs a) {
   for (int cb = 0; cb < NCB; ++cb) {
     const int pos = mb * BM + cb * 16 + r16;
     if (a.sorted_ids[pos] < a.P) {
-      float h[4];
+      float h[4], g4[4], u4[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) h[i] = silu(acc[0][cb][i] * scale) * (acc[1][cb][i] * scale);
+      for (int i = 0; i < 4; ++i) {
+        g4[i] = acc[0][cb][i] * scale;
+        u4[i] = acc[1][cb][i] * scale;
+        h[i] = silu(g4[i]) * u4[i];
+      }
       const size_t idx = (size_t)pos * N + n0 + 4 * g;
-      if (WT == DT_E4M3) {
+      if (a.probe) {
+        probe_store(a, (size_t)pos, n0 + 4 * g, g4, u4);
+      } else if (WT == DT_E4M3) {
         st16(reinterpret_cast<float*>(a.h) + idx,
              i32x4{__float_as_int(h[0]), __float_as_int(h[1]), __float_as_int(h[2]),
                    __float_as_int(h[3])});

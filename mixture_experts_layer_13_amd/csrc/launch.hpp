@@ -56,7 +56,22 @@ struct GemmArgs {
   void* y;               // tile path: [cap, K] expert outputs before the routing
                          // weight, bf16 when the layer output is bf16, else fp32
   void* out;             // [M, K]
+  int probe;             // test builds only: gate/up kernels store the scaled
+                         // gate and up sums ([cap, 2N] fp32: gate | up) in h
+                         // instead of SiLU(gate) * up; the public entry points
+                         // always leave it 0
 };
+
+#ifdef __HIPCC__
+// Probe store of one 4-row MFMA fragment: rows `row` of the [cap, 2N] fp32
+// buffer in a.h, gate values at column col, up values at col + N.
+__device__ __forceinline__ void probe_store(const GemmArgs& a, size_t row, int col, const float g4[4],
+                                            const float u4[4]) {
+  float* p = reinterpret_cast<float*>(a.h) + row * 2 * (size_t)a.N + col;
+  *reinterpret_cast<float4*>(p) = make_float4(g4[0], g4[1], g4[2], g4[3]);
+  *reinterpret_cast<float4*>(p + a.N) = make_float4(u4[0], u4[1], u4[2], u4[3]);
+}
+#endif
 
 int launch_gemm1_stream(const GemmArgs& a, hipStream_t stream);
 bool gemm1_ring_applies(const GemmArgs& a);

@@ -133,6 +133,81 @@ __device__ __forceinline__ void pf_task(int& nt, int& mb) {
   nt = task / nblk, mb = task % nblk;
 }
 
+// Epilogue of a 256 x 128 tile held as 8 x 4 accumulator tiles per wave
+// (wave wr, wc of the 2 x 2 grid).  G1: scale, SiLU(gate) * up, h (bf16, or
+// fp32 plus the running amax for E4M3).  G2: scale * W2 h -> y.
+template <int T, bool G1>
+__device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const f32x4 (&acc)[kPfTA][kPfTB],
+                                            const int (&fe)[kPfTB], int e, int nt, int mb, int wr,
+                                            int wc, int lane) {
+  const int r16 = lane & 15, g = lane >> 4;
+  if constexpr (G1) {
+    float scale = 1.0f;
+    if (T == DT_E4M3) scale = (*a.sx) * a.w13_scale[e];
+    float hmax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kPfTB; ++j) {
+      const int pos = mb * kPfTok + 64 * wc + 16 * j + r16;
+      if (fe[j] < a.P) {
+#pragma unroll
+        for (int i = 0; i < kPfTA / 2; ++i) {
+          float h[4], g4[4], u4[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            g4[t] = acc[i][j][t] * scale;
+            u4[t] = acc[i + kPfTA / 2][j][t] * scale;
+            h[t] = silu(g4[t]) * u4[t];
+          }
+          const int col = nt * 128 + 64 * wr + 16 * i + 4 * g;
+          const size_t idx = (size_t)pos * a.N + col;
+          if (a.probe) {
+            probe_store(a, (size_t)pos, col, g4, u4);
+          } else if (T == DT_E4M3) {
+            st16(reinterpret_cast<float*>(a.h) + idx,
+                 i32x4{__float_as_int(h[0]), __float_as_int(h[1]), __float_as_int(h[2]),
+                       __float_as_int(h[3])});
+#pragma unroll
+            for (int t = 0; t < 4; ++t) hmax = fmaxf(hmax, __builtin_fabsf(h[t]));
+          } else {
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.h) + idx) =
+                make_uint2(f32_to_bf16_bits(h[0]) | (f32_to_bf16_bits(h[1]) << 16),
+                           f32_to_bf16_bits(h[2]) | (f32_to_bf16_bits(h[3]) << 16));
+          }
+        }
+      }
+    }
+    if (T == DT_E4M3) {
+      hmax = wave_max(hmax);
+      if (lane == 0 && hmax > 0.0f) atomicMax(a.hmax_bits, __float_as_uint(hmax));
+    }
+  } else {
+    // y rows hold W2 h of each pair; the routing weight is applied where the
+    // top-k rows of a token are summed.
+    float scale = 1.0f;
+    if (T == DT_E4M3) scale = (*a.sh) * a.w2_scale[e];
+    const bool ybf = a.ot == DT_BF16;
+#pragma unroll
+    for (int j = 0; j < kPfTB; ++j) {
+      const int pos = mb * kPfTok + 64 * wc + 16 * j + r16;
+      if (fe[j] < a.P) {
+#pragma unroll
+        for (int i = 0; i < kPfTA; ++i) {
+          const size_t idx = (size_t)pos * a.K + nt * kPfRows + 128 * wr + 16 * i + 4 * g;
+          const float v[4] = {acc[i][j][0] * scale, acc[i][j][1] * scale, acc[i][j][2] * scale,
+                              acc[i][j][3] * scale};
+          if (ybf)
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + idx) =
+                make_uint2(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+                           f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
+          else
+            st16(reinterpret_cast<float*>(a.y) + idx,
+                 i32x4{__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3])});
+        }
+      }
+    }
+  }
+}
+
 // G1 = true: gate/up product + SiLU * up -> h.  G1 = false: down product
 // -> y (one row per sorted position, routing weight not yet applied).
 template <int T, bool G1>
@@ -331,65 +406,7 @@ __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a) {
   }
   pf_wait_vmcnt<0>();  // no DMA may land after the workgroup's LDS is released
 
-  if constexpr (G1) {
-    float scale = 1.0f;
-    if (T == DT_E4M3) scale = (*a.sx) * a.w13_scale[e];
-    float hmax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kPfTB; ++j) {
-      const int pos = mb * kPfTok + 64 * wc + 16 * j + r16;
-      if (fe[j] < a.P) {
-#pragma unroll
-        for (int i = 0; i < kPfTA / 2; ++i) {
-          float h[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            h[t] = silu(acc[i][j][t] * scale) * (acc[i + kPfTA / 2][j][t] * scale);
-          const size_t idx = (size_t)pos * a.N + nt * 128 + 64 * wr + 16 * i + 4 * g;
-          if (T == DT_E4M3) {
-            st16(reinterpret_cast<float*>(a.h) + idx,
-                 i32x4{__float_as_int(h[0]), __float_as_int(h[1]), __float_as_int(h[2]),
-                       __float_as_int(h[3])});
-#pragma unroll
-            for (int t = 0; t < 4; ++t) hmax = fmaxf(hmax, __builtin_fabsf(h[t]));
-          } else {
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.h) + idx) =
-                make_uint2(f32_to_bf16_bits(h[0]) | (f32_to_bf16_bits(h[1]) << 16),
-                           f32_to_bf16_bits(h[2]) | (f32_to_bf16_bits(h[3]) << 16));
-          }
-        }
-      }
-    }
-    if (T == DT_E4M3) {
-      hmax = wave_max(hmax);
-      if (lane == 0 && hmax > 0.0f) atomicMax(a.hmax_bits, __float_as_uint(hmax));
-    }
-  } else {
-    // y rows hold W2 h of each pair; the routing weight is applied where the
-    // top-k rows of a token are summed.
-    float scale = 1.0f;
-    if (T == DT_E4M3) scale = (*a.sh) * a.w2_scale[e];
-    const bool ybf = a.ot == DT_BF16;
-#pragma unroll
-    for (int j = 0; j < kPfTB; ++j) {
-      const int pos = mb * kPfTok + 64 * wc + 16 * j + r16;
-      if (fe[j] < a.P) {
-#pragma unroll
-        for (int i = 0; i < kPfTA; ++i) {
-          const size_t idx = (size_t)pos * a.K + nt * kPfRows + 128 * wr + 16 * i + 4 * g;
-          const float v[4] = {acc[i][j][0] * scale, acc[i][j][1] * scale, acc[i][j][2] * scale,
-                              acc[i][j][3] * scale};
-          if (ybf)
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + idx) =
-                make_uint2(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
-                           f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
-          else
-            st16(reinterpret_cast<float*>(a.y) + idx,
-                 i32x4{__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3])});
-        }
-      }
-    }
-  }
+  pf_epilogue<T, G1>(a, acc, fe, e, nt, mb, wr, wc, lane);
 }
 
 // The prefill kernels take bf16 x bf16 or E4M3 x E4M3 operands, alignment

@@ -230,7 +230,7 @@ __global__ __launch_bounds__(256) void gemm1_ring_kernel(GemmArgs a) {
     __syncthreads();
     for (int cb = wv; cb < ncb; cb += 4) {
       const int col = c0 + cb * 16 + r16;
-      float h[4];
+      float h[4], g4[4], u4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float gs = 0.0f, us = 0.0f;
@@ -239,9 +239,13 @@ __global__ __launch_bounds__(256) void gemm1_ring_kernel(GemmArgs a) {
           gs += red[((((w * 2 + 0) * NCB + cb) * 4 + i) << 6) + lane];
           us += red[((((w * 2 + 1) * NCB + cb) * 4 + i) << 6) + lane];
         }
-        h[i] = silu(gs * scale) * (us * scale);
+        g4[i] = gs * scale;
+        u4[i] = us * scale;
+        h[i] = silu(g4[i]) * u4[i];
       }
-      if (col < me) {
+      if (a.probe) {
+        if (col < me) probe_store(a, (size_t)(seg0 + col), n0 + 4 * g, g4, u4);
+      } else if (col < me) {
         const size_t idx = (size_t)(seg0 + col) * N + n0 + 4 * g;
         if (WT == DT_E4M3) {
           st16(reinterpret_cast<float*>(a.h) + idx,
