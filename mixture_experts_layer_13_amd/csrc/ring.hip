@@ -179,45 +179,30 @@ __global__ __launch_bounds__(256) void gemm1_ring_kernel(GemmArgs a) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) accg[cb] = accu[cb] = f32x4{0, 0, 0, 0};
 
-    static_assert(D == 4, "prologue and drain written for four stages");
-    R.template issue<0>(0);
-    R.template issue<1>(1);
-    R.template issue<2>(2);
+    // prologue: stages 0 .. D - 2
+    static_for<0, D - 1>([&](auto i) { R.template issue<decltype(i)::value>(decltype(i)::value); });
     // steady state: whole trips of D stages that all refill (ns >= D)
     const int n_issue = ns - (D - 1);  // stages that refill the ring
     int st = 0;
-    for (; st + D <= n_issue; st += D) {
-      R.template body<0, true>(st + 0, ncb, r16, g, accg, accu);
-      R.template body<1, true>(st + 1, ncb, r16, g, accg, accu);
-      R.template body<2, true>(st + 2, ncb, r16, g, accg, accu);
-      R.template body<3, true>(st + 3, ncb, r16, g, accg, accu);
-    }
+    for (; st + D <= n_issue; st += D)
+      static_for<0, D>([&](auto i) {
+        R.template body<decltype(i)::value, true>(st + decltype(i)::value, ncb, r16, g, accg, accu);
+      });
     // the last n_issue % D refilling stages, then D - 1 draining ones; slot =
     // stage % D is static in every branch
-    const int rem = n_issue - st;  // 0..3
-    if (rem == 0) {
-      R.template body<0, false>(st + 0, ncb, r16, g, accg, accu);
-      R.template body<1, false>(st + 1, ncb, r16, g, accg, accu);
-      R.template body<2, false>(st + 2, ncb, r16, g, accg, accu);
-    } else if (rem == 1) {
-      R.template body<0, true>(st + 0, ncb, r16, g, accg, accu);
-      R.template body<1, false>(st + 1, ncb, r16, g, accg, accu);
-      R.template body<2, false>(st + 2, ncb, r16, g, accg, accu);
-      R.template body<3, false>(st + 3, ncb, r16, g, accg, accu);
-    } else if (rem == 2) {
-      R.template body<0, true>(st + 0, ncb, r16, g, accg, accu);
-      R.template body<1, true>(st + 1, ncb, r16, g, accg, accu);
-      R.template body<2, false>(st + 2, ncb, r16, g, accg, accu);
-      R.template body<3, false>(st + 3, ncb, r16, g, accg, accu);
-      R.template body<0, false>(st + 4, ncb, r16, g, accg, accu);
-    } else {
-      R.template body<0, true>(st + 0, ncb, r16, g, accg, accu);
-      R.template body<1, true>(st + 1, ncb, r16, g, accg, accu);
-      R.template body<2, true>(st + 2, ncb, r16, g, accg, accu);
-      R.template body<3, false>(st + 3, ncb, r16, g, accg, accu);
-      R.template body<0, false>(st + 4, ncb, r16, g, accg, accu);
-      R.template body<1, false>(st + 5, ncb, r16, g, accg, accu);
-    }
+    const int rem = n_issue - st;  // 0 .. D - 1
+    static_for<0, D>([&](auto rr) {
+      constexpr int RR = decltype(rr)::value;
+      if (rem == RR) {
+        static_for<0, RR>([&](auto i) {
+          R.template body<decltype(i)::value, true>(st + decltype(i)::value, ncb, r16, g, accg, accu);
+        });
+        static_for<0, D - 1>([&](auto j) {
+          constexpr int J = decltype(j)::value;
+          R.template body<(RR + J) % D, false>(st + RR + J, ncb, r16, g, accg, accu);
+        });
+      }
+    });
 
     // reduce the 4 K-slices (the ring is drained: every body ended with a barrier)
 #pragma unroll
