@@ -208,13 +208,62 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const f32x4 (&acc
   }
 }
 
+// One tile: its coordinates and expert (wave-uniform; readfirstlane keeps
+// them in scalar registers, so that the buffer resources built from them are
+// scalar too) and the per-lane DMA row offsets of its token rows and pair
+// indices of its result columns.  valid = 0: no such tile (its DMA fetches
+// nothing).
+struct PfTile {
+  int nt, mb, e, valid;
+  uint32_t x_voff[kPfXInstr];
+  int fe[kPfTB];  // pair index of the token columns this lane's results belong to
+};
+
+// Tile `task` (nt = task / nvalid, mb = task % nvalid); task < 0 gives an
+// invalid tile.
+template <int T, bool G1>
+__device__ __forceinline__ PfTile pf_tile(const GemmArgs& a, int task, int nvalid, uint32_t rowb,
+                                          int wv, int lane) {
+  PfTile t;
+  t.valid = __builtin_amdgcn_readfirstlane(task >= 0 ? 1 : 0);
+  const int tk = __builtin_amdgcn_readfirstlane(task >= 0 ? task : 0);  // in-range metadata; never fetched
+  t.nt = tk / nvalid;
+  t.mb = tk % nvalid;
+  const int lrow = lane >> 3, pcol = lane & 7, r16 = lane & 15, wc = wv & 1;
+  t.e = __builtin_amdgcn_readfirstlane(a.block_expert[(t.mb * kPfTok) / a.block_m]);
+  int fx[kPfXInstr];  // pair index of the token rows this lane's DMA gathers
+#pragma unroll
+  for (int q = 0; q < kPfXInstr; ++q) fx[q] = a.sorted_ids[t.mb * kPfTok + 8 * (wv * kPfXInstr + q) + lrow];
+#pragma unroll
+  for (int j = 0; j < kPfTB; ++j) t.fe[j] = a.sorted_ids[t.mb * kPfTok + 64 * wc + 16 * j + r16];
+#pragma unroll
+  for (int q = 0; q < kPfXInstr; ++q) {
+    if (G1) {
+      const int r = 8 * (wv * kPfXInstr + q) + lrow;
+      const int f = fx[q] < a.P ? fx[q] : 0;  // padding row: any valid row, never stored
+      t.x_voff[q] = (uint32_t)(f / a.topk) * rowb + pf_logical(r, pcol) * 16;
+    } else {
+      t.x_voff[q] = lrow * rowb + pf_logical(lrow, pcol) * 16;
+    }
+  }
+  return t;
+}
+
 // G1 = true: gate/up product + SiLU * up -> h.  G1 = false: down product
 // -> y (one row per sorted position, routing weight not yet applied).
+//
+// persist = 1: the grid holds one workgroup per CU (a multiple of 8); the
+// valid tiles (ntiles weight tiles x num_padded / 128 token blocks, weight
+// tile major) are split into 8 contiguous ranges, one per XCD, and the
+// workgroups of an XCD take its tiles round-robin.  The DMA ring runs on
+// across tile boundaries: the last three steps of a tile already fetch the
+// first chunks of the next one, and the epilogue of a tile overlaps that
+// fetch.  Needs nchunks >= 3 (and even for E4M3, whose fragments alternate
+// between two register sets per chunk).  persist = 0: one tile per
+// workgroup of an (ntiles, max_blocks) grid.
 template <int T, bool G1>
-__global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a, int ntiles, int persist) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  int nt, mb;
-  pf_task(nt, mb);
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int r16 = lane & 15, g = lane >> 4;
@@ -225,70 +274,69 @@ __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a) {
   const int nchunks = (int)(rowb / kPfChunk);
   const int lrow = lane >> 3, pcol = lane & 7;
 
-  // Metadata, all loads in flight together (every index below is inside the
-  // arrays for any block below max_blocks, valid or not).
-  const int npad = *a.num_padded;
-  const int e = a.block_expert[(mb * kPfTok) / a.block_m];
-  int fx[kPfXInstr];  // pair index of the token rows this lane's DMA gathers
-#pragma unroll
-  for (int q = 0; q < kPfXInstr; ++q) fx[q] = a.sorted_ids[mb * kPfTok + 8 * (wv * kPfXInstr + q) + lrow];
-  int fe[kPfTB];  // pair index of the token columns this lane's results belong to
-#pragma unroll
-  for (int j = 0; j < kPfTB; ++j) fe[j] = a.sorted_ids[mb * kPfTok + 64 * wc + 16 * j + r16];
-  if (mb * kPfTok >= npad) return;  // uniform: past the last block
+  const int nvalid = *a.num_padded / kPfTok;
+  int task, stride, end;
+  if (persist) {
+    const int total = ntiles * nvalid;
+    const int per = total / 8, rem = total % 8;
+    const int xcd = blockIdx.x % 8;
+    task = xcd * per + min(xcd, rem) + blockIdx.x / 8;
+    end = xcd * per + min(xcd, rem) + per + (xcd < rem ? 1 : 0);
+    stride = gridDim.x / 8;
+  } else {
+    int nt, mb;
+    pf_task(nt, mb);
+    if (mb >= nvalid) return;  // uniform: past the last block
+    task = nt * nvalid + mb;
+    end = task + 1;
+    stride = 1;
+  }
+  if (task >= end) return;
 
-  // DMA sources.  A wave's 8 weight instructions cover 64 consecutive tile
-  // rows = 64 consecutive rows of one weight matrix (the gate or up block for
-  // the gate/up product); the rotation only depends on the row mod 8, so one
-  // lane offset serves all of them and the instruction / chunk offsets are
-  // scalar.
-  __amdgpu_buffer_rsrc_t wres, xres;
-  uint32_t w_sbase, x_sbase = 0;
+  PfTile cur = pf_tile<T, G1>(a, task, nvalid, rowb, wv, lane);
+  PfTile nxt = pf_tile<T, G1>(a, task + stride < end ? task + stride : -1, nvalid, rowb, wv, lane);
   const uint32_t w_voff = lrow * rowb + pf_logical(lrow, pcol) * 16;
-  uint32_t x_voff[kPfXInstr];
-  {
+
+  // DMA of chunk cc of the current tile (cc >= nchunks: chunk cc - nchunks
+  // of the next tile) into stage `slot`.  The instructions always issue (the
+  // instruction stream of every chunk is the same); chunks that do not exist
+  // go through a resource of size 0, which fetches nothing.  A wave's 8
+  // weight instructions cover 64 consecutive tile rows = 64 consecutive rows
+  // of one weight matrix (the gate or up block for the gate/up product); the
+  // rotation only depends on the row mod 8, so one lane offset (w_voff)
+  // serves all of them and the instruction and chunk offsets are scalar.
+  auto issue = [&](int cc, int slot) {
+    const bool in_cur = cc < nchunks;
+    const int chunk = in_cur ? cc : cc - nchunks;
+    const bool real = in_cur || (nxt.valid && chunk < nchunks);
+    const int e = in_cur ? cur.e : nxt.e, nt = in_cur ? cur.nt : nxt.nt, mb = in_cur ? cur.mb : nxt.mb;
     const int r0 = 64 * wv;  // first tile row of this wave's weight DMA
+    __amdgpu_buffer_rsrc_t wres, xres;
+    uint32_t w_sb, x_sb = 0;
     if (G1) {
       const int h0 = nt * 128 + 64 * (r0 >> 7);  // first intermediate column
-      wres = pf_rsrc(reinterpret_cast<const char*>(a.w13) + (size_t)e * 2 * a.N * rowb, 2 * a.N * rowb);
-      w_sbase = (uint32_t)((r0 & 127) < 64 ? h0 : a.N + h0) * rowb;
-      xres = pf_rsrc(a.x, (uint32_t)a.M * rowb);
-#pragma unroll
-      for (int q = 0; q < kPfXInstr; ++q) {
-        const int r = 8 * (wv * kPfXInstr + q) + lrow;
-        const int f = fx[q] < a.P ? fx[q] : 0;  // padding row: any valid row, never stored
-        x_voff[q] = (uint32_t)(f / a.topk) * rowb + pf_logical(r, pcol) * 16;
-      }
+      wres = pf_rsrc(reinterpret_cast<const char*>(a.w13) + (size_t)e * 2 * a.N * rowb, real ? 2 * a.N * rowb : 0);
+      w_sb = (uint32_t)((r0 & 127) < 64 ? h0 : a.N + h0) * rowb;
+      xres = pf_rsrc(a.x, real ? (uint32_t)a.M * rowb : 0);
     } else {
-      wres = pf_rsrc(reinterpret_cast<const char*>(a.w2) + (size_t)e * a.K * rowb, a.K * rowb);
-      w_sbase = (uint32_t)(nt * kPfRows + r0) * rowb;
-      xres = pf_rsrc(reinterpret_cast<const char*>(a.hq) + (size_t)mb * kPfTok * rowb, kPfTok * rowb);
-      x_sbase = (uint32_t)(32 * wv) * rowb;
-#pragma unroll
-      for (int q = 0; q < kPfXInstr; ++q) x_voff[q] = lrow * rowb + pf_logical(lrow, pcol) * 16;
+      wres = pf_rsrc(reinterpret_cast<const char*>(a.w2) + (size_t)e * a.K * rowb, real ? a.K * rowb : 0);
+      w_sb = (uint32_t)(nt * kPfRows + r0) * rowb;
+      xres = pf_rsrc(reinterpret_cast<const char*>(a.hq) + (size_t)mb * kPfTok * rowb, real ? kPfTok * rowb : 0);
+      x_sb = (uint32_t)(32 * wv) * rowb;
     }
-  }
-  const __amdgpu_buffer_rsrc_t null_res = pf_rsrc(a.x, 0);  // every access out of range
-
-  // DMA of `chunk` into stage `slot`; past the last chunk the instructions
-  // still issue (the instruction stream of every chunk is the same) through a
-  // resource of size 0, which fetches nothing.
-  auto issue = [&](int chunk, int slot) {
-    const bool real = chunk < nchunks;
-    const __amdgpu_buffer_rsrc_t wr_ = real ? wres : null_res;
-    const __amdgpu_buffer_rsrc_t xr_ = real ? xres : null_res;
     char* sb = lds + slot * kPfStageBytes;
     const uint32_t off = (uint32_t)chunk * kPfChunk;
 #pragma unroll
     for (int q = 0; q < kPfWInstr; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          wr_, (__attribute__((address_space(3))) void*)(sb + (wv * kPfWInstr + q) * 1024), 16, w_voff,
-          w_sbase + (uint32_t)(8 * q) * rowb + off, 0, kPfAux);
+          wres, (__attribute__((address_space(3))) void*)(sb + (wv * kPfWInstr + q) * 1024), 16, w_voff,
+          w_sb + (uint32_t)(8 * q) * rowb + off, 0, kPfAux);
 #pragma unroll
     for (int q = 0; q < kPfXInstr; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xr_, (__attribute__((address_space(3))) void*)(sb + kPfWBytes + (wv * kPfXInstr + q) * 1024),
-          16, x_voff[q], x_sbase + (uint32_t)(8 * q) * (G1 ? 0u : rowb) + off, 0, kPfAux);
+          xres, (__attribute__((address_space(3))) void*)(sb + kPfWBytes + (wv * kPfXInstr + q) * 1024), 16,
+          in_cur ? cur.x_voff[q] : nxt.x_voff[q], x_sb + (uint32_t)(8 * q) * (G1 ? 0u : rowb) + off, 0,
+          kPfAux);
   };
 
   // The empty asm makes each zero accumulator an opaque value of its own:
@@ -296,13 +344,16 @@ __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a) {
   // first iteration and then shuffles accumulators between registers inside
   // the loop.
   f32x4 acc[kPfTA][kPfTB];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int i = 0; i < kPfTA; ++i)
+    for (int i = 0; i < kPfTA; ++i)
 #pragma unroll
-    for (int j = 0; j < kPfTB; ++j) {
-      acc[i][j] = f32x4{0, 0, 0, 0};
-      asm volatile("" : "+a"(acc[i][j]));
-    }
+      for (int j = 0; j < kPfTB; ++j) {
+        acc[i][j] = f32x4{0, 0, 0, 0};
+        asm volatile("" : "+a"(acc[i][j]));
+      }
+  };
+  zero_acc();
 
   // LDS offsets of this lane's fragments (logical columns g and g + 4); tile
   // i adds i * 16 rows = i * 2048 bytes (the rotation repeats every 8 rows)
@@ -319,16 +370,16 @@ __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a) {
   pf_wait_vmcnt<2 * kPfNI>();
   pf_barrier();
 
+  int q0 = 0;  // ring position of the current tile's chunk 0 (mod 3)
   if constexpr (T == DT_BF16) {
     // bf16: a chunk is two K halves of 32 (16-byte columns g and g + 4 of
-    // each row); half 0 of chunk c is in registers when iteration c starts.
+    // each row); half 0 of chunk c is in registers when step c starts:
     //   multiply half 0 while reading half 1 of chunk c;
     //   wait for chunk c + 1, barrier (every wave holds all of chunk c, so
-    //   stage c % 3 is free), refill it with chunk c + 3;
-    //   multiply half 1 while reading half 0 of chunk c + 1.
-    // Each register set keeps one role, so the loop body is straight-line
-    // code; the last iteration reads a stale stage and the DMA past the end
-    // fetches nothing, so every iteration is the same.
+    //   its stage is free), refill it with chunk c + 3;
+    //   multiply half 1 while reading half 0 of chunk c + 1 (of the next tile
+    //   after the last chunk).
+    // Each register set keeps one role, so the loop body is straight-line.
     i32x4 A0[kPfTA], B0[kPfTB], A1[kPfTA], B1[kPfTB];
     auto load_half = [&](int h, int slot, i32x4 (&A)[kPfTA], i32x4 (&B)[kPfTB]) {
       const char* sb = lds + slot * kPfStageBytes;
@@ -346,22 +397,31 @@ __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a) {
                                                               0, 0, 0);
     };
     load_half(0, 0, A0, B0);
-    for (int c = 0; c < nchunks; ++c) {
-      const int slot = c % 3;
-      load_half(1, slot, A1, B1);
-      mult_half(A0, B0);
-      pf_interleave_half<kPfTA * kPfTB, false>();
-      pf_wait_vmcnt<kPfNI>();
-      pf_barrier();
-      issue(c + 3, slot);
-      load_half(0, slot == 2 ? 0 : slot + 1, A0, B0);
-      mult_half(A1, B1);
-      pf_interleave_half<kPfTA * kPfTB, true>();
+    while (true) {
+      for (int c = 0; c < nchunks; ++c) {
+        const int slot = (q0 + c) % 3;
+        load_half(1, slot, A1, B1);
+        mult_half(A0, B0);
+        pf_interleave_half<kPfTA * kPfTB, false>();
+        pf_wait_vmcnt<kPfNI>();
+        pf_barrier();
+        issue(c + 3, slot);
+        load_half(0, slot == 2 ? 0 : slot + 1, A0, B0);
+        mult_half(A1, B1);
+        pf_interleave_half<kPfTA * kPfTB, true>();
+      }
+      pf_epilogue<T, G1>(a, acc, cur.fe, cur.e, cur.nt, cur.mb, wr, wc, lane);
+      task += stride;
+      if (task >= end) break;
+      q0 = (q0 + nchunks) % 3;
+      cur = nxt;
+      nxt = pf_tile<T, G1>(a, task + stride < end ? task + stride : -1, nvalid, rowb, wv, lane);
+      zero_acc();
     }
   } else {
     // E4M3: one MFMA takes a whole 128-byte chunk, so whole chunks are
     // double-buffered: fragments of chunk c are read right after the barrier
-    // that publishes it and multiplied one iteration later.
+    // that publishes it and multiplied one step later.
     Raw<T> A0[kPfTA], B0[kPfTB], A1[kPfTA], B1[kPfTB];
     auto load_frags = [&](int slot, Raw<T> (&A)[kPfTA], Raw<T> (&B)[kPfTB]) {
       const char* sb = lds + slot * kPfStageBytes;
@@ -379,34 +439,37 @@ __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < kPfTB; ++j) acc[i][j] = mma(to_op<T>(A[i]), to_op<T>(B[j]), acc[i][j]);
     };
-    // Iteration c: wait for chunk c + 1, barrier (chunk c + 1 visible; every
-    // wave holds chunk c's fragments, so stage c % 3 is free), refill that
-    // stage with chunk c + 3, read chunk c + 1's fragments, multiply chunk c.
+    // Step c: wait for chunk c + 1, barrier (chunk c + 1 visible; every wave
+    // holds chunk c's fragments, so its stage is free), refill that stage
+    // with chunk c + 3, read chunk c + 1's fragments, multiply chunk c.
     auto step = [&](int c, Raw<T> (&Ac)[kPfTA], Raw<T> (&Bc)[kPfTB], Raw<T> (&An)[kPfTA],
                     Raw<T> (&Bn)[kPfTB]) {
+      const int slot = (q0 + c) % 3;
       pf_wait_vmcnt<kPfNI>();
       pf_barrier();
-      issue(c + 3, c % 3);
-      load_frags((c + 1) % 3, An, Bn);
+      issue(c + 3, slot);
+      load_frags(slot == 2 ? 0 : slot + 1, An, Bn);
       compute(Ac, Bc);
       pf_interleave<kPfMfma<T>()>();
     };
     load_frags(0, A0, B0);
-    int c = 0;
-    for (; c + 2 < nchunks; c += 2) {
-      step(c, A0, B0, A1, B1);
-      step(c + 1, A1, B1, A0, B0);
-    }
-    if (c + 1 < nchunks) {  // two chunks left
-      step(c, A0, B0, A1, B1);
-      compute(A1, B1);
-    } else {  // one chunk left
-      compute(A0, B0);
+    while (true) {
+      int c = 0;
+      for (; c + 1 < nchunks; c += 2) {
+        step(c, A0, B0, A1, B1);
+        step(c + 1, A1, B1, A0, B0);
+      }
+      if (c < nchunks) step(c, A0, B0, A1, B1);  // odd count: one tile per workgroup only
+      pf_epilogue<T, G1>(a, acc, cur.fe, cur.e, cur.nt, cur.mb, wr, wc, lane);
+      task += stride;
+      if (task >= end) break;
+      q0 = (q0 + nchunks) % 3;
+      cur = nxt;
+      nxt = pf_tile<T, G1>(a, task + stride < end ? task + stride : -1, nvalid, rowb, wv, lane);
+      zero_acc();
     }
   }
   pf_wait_vmcnt<0>();  // no DMA may land after the workgroup's LDS is released
-
-  pf_epilogue<T, G1>(a, acc, fe, e, nt, mb, wr, wc, lane);
 }
 
 // The prefill kernels take bf16 x bf16 or E4M3 x E4M3 operands, alignment
@@ -423,6 +486,23 @@ bool pf_applies(const GemmArgs& a, bool gemm1) {
   return gemm1 ? (a.N % 128 == 0) : (a.K % kPfRows == 0);
 }
 
+// Workgroups of a persistent launch: one per CU (the 144 KiB of LDS admit
+// one), but at most a quarter of the tile count (small problems still give
+// every workgroup a run of tiles), in multiples of the 8 XCDs; 0 = too few
+// tiles for a persistent launch.
+static int pf_persistent_grid(long long tiles) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n = 256;
+    cus = n;
+  }
+  long long g = tiles / 4 < cus ? tiles / 4 : cus;
+  return (int)(g / 8 * 8);
+}
+
 template <int T, bool G1>
 static int pf_launch(const GemmArgs& a, hipStream_t st) {
   static bool attr_set = false;  // per process: one device's attribute covers the kernel
@@ -433,8 +513,17 @@ static int pf_launch(const GemmArgs& a, hipStream_t st) {
     attr_set = true;
   }
   const int ntiles = G1 ? a.N / 128 : a.K / kPfRows;
-  dim3 grid(ntiles, a.max_blocks);  // block_m >= 128: max_blocks counts 128-row tiles
-  hipLaunchKernelGGL((pf_gemm_kernel<T, G1>), grid, dim3(kPfThreads), kPfLdsBytes, st, a);
+  const long long rowb = (long long)(G1 ? a.K : a.N) * Family<T>::kBytes;
+  const int nchunks = (int)(rowb / kPfChunk);
+  const int persist = nchunks >= 3 && (T != DT_E4M3 || nchunks % 2 == 0);
+  const long long tasks = (long long)ntiles * a.max_blocks;  // block_m >= 128: 128-row tiles
+  const int pgrid = persist ? pf_persistent_grid(tasks) : 0;
+  if (pgrid > 0) {
+    hipLaunchKernelGGL((pf_gemm_kernel<T, G1>), dim3(pgrid), dim3(kPfThreads), kPfLdsBytes, st, a, ntiles, 1);
+  } else {
+    dim3 grid(ntiles, a.max_blocks);
+    hipLaunchKernelGGL((pf_gemm_kernel<T, G1>), grid, dim3(kPfThreads), kPfLdsBytes, st, a, ntiles, 0);
+  }
   return (int)hipGetLastError();
 }
 

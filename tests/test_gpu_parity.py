@@ -204,6 +204,11 @@ PREFILL_SMALL = [
     ("fp8_T130_K640", "decode_fp8", 130, 640, 384, 8, 2, 128),
     ("bf16_T129_I128", "decode_bf16", 129, 768, 128, 8, 4, 256),
     ("bf16_T520_E4", "decode_bf16", 520, 512, 256, 4, 2, 128),
+    # persistent launches: runs of several tiles per workgroup, the DMA ring
+    # carried across tile boundaries (8-16 chunks of K, 104 tiles)
+    ("bf16_T600_persist", "decode_bf16", 600, 1024, 512, 8, 4, 128),
+    ("fp8_T600_persist", "decode_fp8", 600, 1024, 512, 8, 4, 128),
+    ("fp8_T700_persist_bm256", "large_fp8", 700, 1024, 512, 16, 4, 256),
 ]
 
 
