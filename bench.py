@@ -238,7 +238,7 @@ def main():
                    "active_experts": U, "kernel_family": "stream" if stream_path else "tile"},
         "op_hbm_gbps": round(op_bytes / (ms_step * 1e-3) / 1e9, 1),
         "op_tflops": round(flops / (ms_step * 1e-3) / 1e12, 3),
-        "gemm2_avg_launch_us": round(g2_ms * 1e3, 2),
+        "down_gemm_avg_launch_us": round(g2_ms * 1e3, 2),
         "timing": "K steps captured in one HIP graph, replayed between synchronisations; "
                   "kernel durations from HIP events on an eager pass queued behind a replay",
         "roofline": roof,

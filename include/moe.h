@@ -227,7 +227,8 @@ moe_status moe_quantize_act(const void* x, int32_t x_dtype, int64_t n,
  * Measurement hook.  When set, the next moe_fused_forward call on this
  * thread records events[0]/events[1] (hipEvent_t) on its stream right
  * before and after the gate/up GEMM kernel, and events[2]/events[3] around
- * the down GEMM (and, for M > 64, the combine kernel); the hook is then
+ * the down GEMM kernel (for M <= 64 that kernel also does the combine; for
+ * M > 64 the combine kernel runs after events[3]); the hook is then
  * cleared.  NULL entries are skipped.  Meant for eager (uncaptured)
  * calls.  Host only; no effect on results.
  */

@@ -336,6 +336,8 @@ moe_status moe_fused_forward(const moe_problem* p, const void* a, const void* w1
   } else {
     err = moe::launch_gemm2_tile(g, st);
     if (err) return hip_status(err, "down GEMM launch");
+    if (prof[3]) (void)hipEventRecord((hipEvent_t)prof[3], st);
+    prof[3] = nullptr;
     err = moe::launch_combine(g, st);
     if (err) return hip_status(err, "combine launch");
   }

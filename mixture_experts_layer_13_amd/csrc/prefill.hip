@@ -21,11 +21,11 @@
 // assignment and rotation reads at the linear-access rate, while the
 // assignment 2g, 2g + 1 is two-way bank-conflicted under every swizzle tried.
 //
-// Workgroup: 4 waves (one per SIMD) as 2 (weight rows) x 2 (tokens); each
-// wave owns a 128 x 64 sub-tile = 8 x 4 MFMA tiles of 16 x 16, whose
-// accumulators live in the accumulation registers, and double-buffers its
-// operand fragments in registers.  For the gate/up product the 128 rows of a
-// wave are 64 gate rows followed by the 64 up rows of the same intermediate
+// Workgroup: WR (weight rows) x 2 (tokens) waves -- 4 x 2 waves of 64 x 64
+// (two per SIMD) or 2 x 2 of 128 x 64 (one per SIMD, E4M3 gate/up) -- each
+// with its accumulators in the accumulation registers and its operand
+// fragments double-buffered in registers.  For the gate/up product a wave's
+// rows are gate rows followed by the up rows of the same intermediate
 // columns, so SiLU(gate) * up is formed in registers.
 #include "common.hpp"
 #include "launch.hpp"
@@ -40,13 +40,29 @@ constexpr int kPfWBytes = kPfRows * kPfChunk;         // 32 KiB
 constexpr int kPfXBytes = kPfTok * kPfChunk;          // 16 KiB
 constexpr int kPfStageBytes = kPfWBytes + kPfXBytes;  // 48 KiB
 constexpr int kPfLdsBytes = kPfStages * kPfStageBytes;
-constexpr int kPfThreads = 256;
-constexpr int kPfWaves = kPfThreads / kWave;
-constexpr int kPfWInstr = kPfWBytes / 1024 / kPfWaves;  // 8 DMA instructions per wave
-constexpr int kPfXInstr = kPfXBytes / 1024 / kPfWaves;  // 4
-constexpr int kPfTA = 8;  // 16-row weight tiles per wave
-constexpr int kPfTB = 4;  // 16-row token tiles per wave
-constexpr int kPfNI = kPfWInstr + kPfXInstr;
+// Wave layout of a workgroup: WR waves along the weight rows x 2 along the
+// token rows; each wave owns (256 / WR) x 64 of the tile.
+template <int WR>
+struct PfL {
+  static constexpr int WC = 2;
+  static constexpr int Waves = WR * WC;
+  static constexpr int Threads = Waves * kWave;
+  static constexpr int WaveRows = kPfRows / WR;          // weight rows of one wave
+  static constexpr int WaveTok = kPfTok / WC;            // token rows of one wave
+  static constexpr int WInstr = kPfWBytes / 1024 / Waves;  // DMA instructions per wave and chunk
+  static constexpr int XInstr = kPfXBytes / 1024 / Waves;
+  static constexpr int WDmaRows = kPfRows / Waves;       // tile rows of one wave's weight DMA
+  static constexpr int XDmaRows = kPfTok / Waves;
+  static constexpr int TA = WaveRows / 16;               // 16-row weight tiles per wave
+  static constexpr int TB = WaveTok / 16;                // 16-row token tiles per wave
+  static constexpr int NI = WInstr + XInstr;
+  static constexpr int Ds = 2 * (TA + TB);               // fragment reads per chunk and wave
+  template <int T>
+  static constexpr int mfma() {                          // MFMAs per chunk and wave
+    return TA * TB * (T == DT_E4M3 ? 1 : 2);
+  }
+};
+
 constexpr int kPfAux = 0;  // cache policy of the DMA (operands are re-read by other tiles)
 
 // LDS offset of logical 16-byte column c of row r (see the header), and the
@@ -71,44 +87,39 @@ __device__ __forceinline__ void pf_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// MFMA instructions per chunk and wave.
-template <int T>
-constexpr int kPfMfma() {
-  return kPfTA * kPfTB * (T == DT_E4M3 ? 1 : 2);
-}
-constexpr int kPfDs = 2 * (kPfTA + kPfTB);  // fragment reads per chunk and wave
-
-// Scheduling of one chunk's instruction stream: the kPfNI DMA instructions of
-// chunk c + 3 and the kPfDs fragment reads of chunk c + 1 are spread over the
+// Scheduling of one chunk's instruction stream: the NI DMA instructions of
+// chunk c + 3 and the Ds fragment reads of chunk c + 1 are spread over the
 // first three quarters of chunk c's MFMAs (a few MFMAs, one read, one DMA
 // instruction, ...), so that they issue in the MFMAs' shadow and the reads
 // have completed by the next barrier.  sched_group_barrier masks: 0x008 MFMA,
 // 0x100 DS read, 0x020 VMEM read.
-template <int NMF, int I = 0>
+template <int WR, int NMF, int I = 0>
 __device__ __forceinline__ void pf_interleave() {
-  constexpr int per = (NMF * 3 / 4) / kPfDs;  // MFMAs before each read
-  if constexpr (I < kPfDs) {
+  using L = PfL<WR>;
+  constexpr int per = (NMF * 3 / 4) / L::Ds;  // MFMAs before each read
+  if constexpr (I < L::Ds) {
     __builtin_amdgcn_sched_group_barrier(0x008, per, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    if constexpr (I < kPfNI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    pf_interleave<NMF, I + 1>();
+    if constexpr (I < L::NI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    pf_interleave<WR, NMF, I + 1>();
   } else {
-    __builtin_amdgcn_sched_group_barrier(0x008, NMF - per * kPfDs, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NMF - per * L::Ds, 0);
   }
 }
 
-// Scheduling of one bf16 half chunk: its NMF MFMAs with the kPfDs / 2
-// fragment reads of the next half spread over the first three quarters, and
-// (second half) the kPfNI DMA instructions of the refill as well.
-template <int NMF, bool DMA, int I = 0>
+// Scheduling of one bf16 half chunk: its NMF MFMAs with the Ds / 2 fragment
+// reads of the next half spread over the first three quarters, and (second
+// half) the NI DMA instructions of the refill as well.
+template <int WR, int NMF, bool DMA, int I = 0>
 __device__ __forceinline__ void pf_interleave_half() {
-  constexpr int nds = kPfDs / 2;
+  using L = PfL<WR>;
+  constexpr int nds = L::Ds / 2;
   constexpr int per = (NMF * 3 / 4) / nds;
   if constexpr (I < nds) {
     __builtin_amdgcn_sched_group_barrier(0x008, per, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    if constexpr (DMA && I < kPfNI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    pf_interleave_half<NMF, DMA, I + 1>();
+    if constexpr (DMA && I < L::NI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    pf_interleave_half<WR, NMF, DMA, I + 1>();
   } else {
     __builtin_amdgcn_sched_group_barrier(0x008, NMF - per * nds, 0);
   }
@@ -136,29 +147,31 @@ __device__ __forceinline__ void pf_task(int& nt, int& mb) {
 // Epilogue of a 256 x 128 tile held as 8 x 4 accumulator tiles per wave
 // (wave wr, wc of the 2 x 2 grid).  G1: scale, SiLU(gate) * up, h (bf16, or
 // fp32 plus the running amax for E4M3).  G2: scale * W2 h -> y.
-template <int T, bool G1>
-__device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const f32x4 (&acc)[kPfTA][kPfTB],
-                                            const int (&fe)[kPfTB], int e, int nt, int mb, int wr,
+template <int T, bool G1, int WR>
+__device__ __forceinline__ void pf_epilogue(const GemmArgs& a,
+                                            const f32x4 (&acc)[PfL<WR>::TA][PfL<WR>::TB],
+                                            const int (&fe)[PfL<WR>::TB], int e, int nt, int mb, int wr,
                                             int wc, int lane) {
+  using L = PfL<WR>;
   const int r16 = lane & 15, g = lane >> 4;
   if constexpr (G1) {
     float scale = 1.0f;
     if (T == DT_E4M3) scale = (*a.sx) * a.w13_scale[e];
     float hmax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kPfTB; ++j) {
-      const int pos = mb * kPfTok + 64 * wc + 16 * j + r16;
+    for (int j = 0; j < L::TB; ++j) {
+      const int pos = mb * kPfTok + L::WaveTok * wc + 16 * j + r16;
       if (fe[j] < a.P) {
 #pragma unroll
-        for (int i = 0; i < kPfTA / 2; ++i) {
+        for (int i = 0; i < L::TA / 2; ++i) {
           float h[4], g4[4], u4[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             g4[t] = acc[i][j][t] * scale;
-            u4[t] = acc[i + kPfTA / 2][j][t] * scale;
+            u4[t] = acc[i + L::TA / 2][j][t] * scale;
             h[t] = silu(g4[t]) * u4[t];
           }
-          const int col = nt * 128 + 64 * wr + 16 * i + 4 * g;
+          const int col = nt * 128 + (L::WaveRows / 2) * wr + 16 * i + 4 * g;
           const size_t idx = (size_t)pos * a.N + col;
           if (a.probe) {
             probe_store(a, (size_t)pos, col, g4, u4);
@@ -187,12 +200,12 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const f32x4 (&acc
     if (T == DT_E4M3) scale = (*a.sh) * a.w2_scale[e];
     const bool ybf = a.ot == DT_BF16;
 #pragma unroll
-    for (int j = 0; j < kPfTB; ++j) {
-      const int pos = mb * kPfTok + 64 * wc + 16 * j + r16;
+    for (int j = 0; j < L::TB; ++j) {
+      const int pos = mb * kPfTok + L::WaveTok * wc + 16 * j + r16;
       if (fe[j] < a.P) {
 #pragma unroll
-        for (int i = 0; i < kPfTA; ++i) {
-          const size_t idx = (size_t)pos * a.K + nt * kPfRows + 128 * wr + 16 * i + 4 * g;
+        for (int i = 0; i < L::TA; ++i) {
+          const size_t idx = (size_t)pos * a.K + nt * kPfRows + L::WaveRows * wr + 16 * i + 4 * g;
           const float v[4] = {acc[i][j][0] * scale, acc[i][j][1] * scale, acc[i][j][2] * scale,
                               acc[i][j][3] * scale};
           if (ybf)
@@ -213,33 +226,37 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const f32x4 (&acc
 // scalar too) and the per-lane DMA row offsets of its token rows and pair
 // indices of its result columns.  valid = 0: no such tile (its DMA fetches
 // nothing).
+template <int WR>
 struct PfTile {
   int nt, mb, e, valid;
-  uint32_t x_voff[kPfXInstr];
-  int fe[kPfTB];  // pair index of the token columns this lane's results belong to
+  uint32_t x_voff[PfL<WR>::XInstr];
+  int fe[PfL<WR>::TB];  // pair index of the token columns this lane's results belong to
 };
 
-// Tile `task` (nt = task / nvalid, mb = task % nvalid); task < 0 gives an
-// invalid tile.
-template <int T, bool G1>
-__device__ __forceinline__ PfTile pf_tile(const GemmArgs& a, int task, int nvalid, uint32_t rowb,
-                                          int wv, int lane) {
-  PfTile t;
+// Tile `task`, in token block major order (mb = task / ntiles, nt = task %
+// ntiles: the weight tiles that share one token block are neighbours, which
+// measured slightly faster on MI355X than weight tile major); task < 0 gives
+// an invalid tile.
+template <int T, bool G1, int WR>
+__device__ __forceinline__ PfTile<WR> pf_tile(const GemmArgs& a, int task, int ntiles,
+                                              uint32_t rowb, int wv, int lane) {
+  using L = PfL<WR>;
+  PfTile<WR> t;
   t.valid = __builtin_amdgcn_readfirstlane(task >= 0 ? 1 : 0);
   const int tk = __builtin_amdgcn_readfirstlane(task >= 0 ? task : 0);  // in-range metadata; never fetched
-  t.nt = tk / nvalid;
-  t.mb = tk % nvalid;
-  const int lrow = lane >> 3, pcol = lane & 7, r16 = lane & 15, wc = wv & 1;
+  t.mb = tk / ntiles;
+  t.nt = tk % ntiles;
+  const int lrow = lane >> 3, pcol = lane & 7, r16 = lane & 15, wc = wv % L::WC;
   t.e = __builtin_amdgcn_readfirstlane(a.block_expert[(t.mb * kPfTok) / a.block_m]);
-  int fx[kPfXInstr];  // pair index of the token rows this lane's DMA gathers
+  int fx[L::XInstr];  // pair index of the token rows this lane's DMA gathers
 #pragma unroll
-  for (int q = 0; q < kPfXInstr; ++q) fx[q] = a.sorted_ids[t.mb * kPfTok + 8 * (wv * kPfXInstr + q) + lrow];
+  for (int q = 0; q < L::XInstr; ++q) fx[q] = a.sorted_ids[t.mb * kPfTok + 8 * (wv * L::XInstr + q) + lrow];
 #pragma unroll
-  for (int j = 0; j < kPfTB; ++j) t.fe[j] = a.sorted_ids[t.mb * kPfTok + 64 * wc + 16 * j + r16];
+  for (int j = 0; j < L::TB; ++j) t.fe[j] = a.sorted_ids[t.mb * kPfTok + L::WaveTok * wc + 16 * j + r16];
 #pragma unroll
-  for (int q = 0; q < kPfXInstr; ++q) {
+  for (int q = 0; q < L::XInstr; ++q) {
     if (G1) {
-      const int r = 8 * (wv * kPfXInstr + q) + lrow;
+      const int r = 8 * (wv * L::XInstr + q) + lrow;
       const int f = fx[q] < a.P ? fx[q] : 0;  // padding row: any valid row, never stored
       t.x_voff[q] = (uint32_t)(f / a.topk) * rowb + pf_logical(r, pcol) * 16;
     } else {
@@ -249,25 +266,76 @@ __device__ __forceinline__ PfTile pf_tile(const GemmArgs& a, int task, int nvali
   return t;
 }
 
+// DMA of chunk cc of the current tile (cc >= nchunks: chunk cc - nchunks
+// of the next tile) into stage `slot`.  The instructions always issue (the
+// instruction stream of every chunk is the same); chunks that do not exist
+// go through a resource of size 0, which fetches nothing.  A wave's WInstr
+// weight instructions cover WDmaRows consecutive tile rows, which are
+// consecutive rows of one weight matrix (for the gate/up product all gate or
+// all up rows, as WDmaRows is at most half a wave's rows); the rotation only
+// depends on the row mod 8, so one lane offset (w_voff) serves all of them
+// and the instruction and chunk offsets are scalar.
+template <int T, bool G1, int WR>
+__device__ __forceinline__ void pf_issue(const GemmArgs& a, char* lds, const PfTile<WR>& cur,
+                                         const PfTile<WR>& nxt, int cc, int slot, int nchunks,
+                                         uint32_t rowb, uint32_t w_voff, int wv) {
+  using L = PfL<WR>;
+  const bool in_cur = cc < nchunks;
+  const int chunk = in_cur ? cc : cc - nchunks;
+  const bool real = in_cur || (nxt.valid && chunk < nchunks);
+  const int e = in_cur ? cur.e : nxt.e, nt = in_cur ? cur.nt : nxt.nt, mb = in_cur ? cur.mb : nxt.mb;
+  const int r0 = L::WDmaRows * wv;  // first tile row of this wave's weight DMA
+  __amdgpu_buffer_rsrc_t wres, xres;
+  uint32_t w_sb, x_sb = 0;
+  if (G1) {
+    // wave rows: L::WaveRows / 2 gate rows, then the up rows of the same columns
+    constexpr int half = L::WaveRows / 2;
+    const int within = r0 % L::WaveRows;
+    const int h0 = nt * 128 + half * (r0 / L::WaveRows);  // first intermediate column
+    wres = pf_rsrc(reinterpret_cast<const char*>(a.w13) + (size_t)e * 2 * a.N * rowb, real ? 2 * a.N * rowb : 0);
+    w_sb = (uint32_t)(within < half ? h0 + within : a.N + h0 + within - half) * rowb;
+    xres = pf_rsrc(a.x, real ? (uint32_t)a.M * rowb : 0);
+  } else {
+    wres = pf_rsrc(reinterpret_cast<const char*>(a.w2) + (size_t)e * a.K * rowb, real ? a.K * rowb : 0);
+    w_sb = (uint32_t)(nt * kPfRows + r0) * rowb;
+    xres = pf_rsrc(reinterpret_cast<const char*>(a.hq) + (size_t)mb * kPfTok * rowb, real ? kPfTok * rowb : 0);
+    x_sb = (uint32_t)(L::XDmaRows * wv) * rowb;
+  }
+  char* sb = lds + slot * kPfStageBytes;
+  const uint32_t off = (uint32_t)chunk * kPfChunk;
+#pragma unroll
+  for (int q = 0; q < L::WInstr; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        wres, (__attribute__((address_space(3))) void*)(sb + (wv * L::WInstr + q) * 1024), 16, w_voff,
+        w_sb + (uint32_t)(8 * q) * rowb + off, 0, kPfAux);
+#pragma unroll
+  for (int q = 0; q < L::XInstr; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        xres, (__attribute__((address_space(3))) void*)(sb + kPfWBytes + (wv * L::XInstr + q) * 1024), 16,
+        in_cur ? cur.x_voff[q] : nxt.x_voff[q], x_sb + (uint32_t)(8 * q) * (G1 ? 0u : rowb) + off, 0,
+        kPfAux);
+}
+
 // G1 = true: gate/up product + SiLU * up -> h.  G1 = false: down product
 // -> y (one row per sorted position, routing weight not yet applied).
 //
 // persist = 1: the grid holds one workgroup per CU (a multiple of 8); the
-// valid tiles (ntiles weight tiles x num_padded / 128 token blocks, weight
-// tile major) are split into 8 contiguous ranges, one per XCD, and the
+// valid tiles (ntiles weight tiles x num_padded / 128 token blocks, in
+// pf_tile's order) are split into 8 contiguous ranges, one per XCD, and the
 // workgroups of an XCD take its tiles round-robin.  The DMA ring runs on
 // across tile boundaries: the last three steps of a tile already fetch the
 // first chunks of the next one, and the epilogue of a tile overlaps that
 // fetch.  Needs nchunks >= 3 (and even for E4M3, whose fragments alternate
 // between two register sets per chunk).  persist = 0: one tile per
 // workgroup of an (ntiles, max_blocks) grid.
-template <int T, bool G1>
-__global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a, int ntiles, int persist) {
+template <int T, bool G1, int WR>
+__global__ __launch_bounds__(PfL<WR>::Threads) void pf_gemm_kernel(GemmArgs a, int ntiles, int persist) {
+  using L = PfL<WR>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int r16 = lane & 15, g = lane >> 4;
-  const int wr = wv >> 1, wc = wv & 1;
+  const int wr = wv / L::WC, wc = wv % L::WC;
   const int Kd = G1 ? a.K : a.N;  // contraction length
   constexpr int EB = Family<T>::kBytes;
   const uint32_t rowb = (uint32_t)Kd * EB;
@@ -287,68 +355,30 @@ __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a, int nti
     int nt, mb;
     pf_task(nt, mb);
     if (mb >= nvalid) return;  // uniform: past the last block
-    task = nt * nvalid + mb;
+    task = mb * ntiles + nt;
     end = task + 1;
     stride = 1;
   }
   if (task >= end) return;
 
-  PfTile cur = pf_tile<T, G1>(a, task, nvalid, rowb, wv, lane);
-  PfTile nxt = pf_tile<T, G1>(a, task + stride < end ? task + stride : -1, nvalid, rowb, wv, lane);
+  PfTile<WR> cur = pf_tile<T, G1, WR>(a, task, ntiles, rowb, wv, lane);
+  PfTile<WR> nxt = pf_tile<T, G1, WR>(a, task + stride < end ? task + stride : -1, ntiles, rowb, wv, lane);
   const uint32_t w_voff = lrow * rowb + pf_logical(lrow, pcol) * 16;
 
-  // DMA of chunk cc of the current tile (cc >= nchunks: chunk cc - nchunks
-  // of the next tile) into stage `slot`.  The instructions always issue (the
-  // instruction stream of every chunk is the same); chunks that do not exist
-  // go through a resource of size 0, which fetches nothing.  A wave's 8
-  // weight instructions cover 64 consecutive tile rows = 64 consecutive rows
-  // of one weight matrix (the gate or up block for the gate/up product); the
-  // rotation only depends on the row mod 8, so one lane offset (w_voff)
-  // serves all of them and the instruction and chunk offsets are scalar.
   auto issue = [&](int cc, int slot) {
-    const bool in_cur = cc < nchunks;
-    const int chunk = in_cur ? cc : cc - nchunks;
-    const bool real = in_cur || (nxt.valid && chunk < nchunks);
-    const int e = in_cur ? cur.e : nxt.e, nt = in_cur ? cur.nt : nxt.nt, mb = in_cur ? cur.mb : nxt.mb;
-    const int r0 = 64 * wv;  // first tile row of this wave's weight DMA
-    __amdgpu_buffer_rsrc_t wres, xres;
-    uint32_t w_sb, x_sb = 0;
-    if (G1) {
-      const int h0 = nt * 128 + 64 * (r0 >> 7);  // first intermediate column
-      wres = pf_rsrc(reinterpret_cast<const char*>(a.w13) + (size_t)e * 2 * a.N * rowb, real ? 2 * a.N * rowb : 0);
-      w_sb = (uint32_t)((r0 & 127) < 64 ? h0 : a.N + h0) * rowb;
-      xres = pf_rsrc(a.x, real ? (uint32_t)a.M * rowb : 0);
-    } else {
-      wres = pf_rsrc(reinterpret_cast<const char*>(a.w2) + (size_t)e * a.K * rowb, real ? a.K * rowb : 0);
-      w_sb = (uint32_t)(nt * kPfRows + r0) * rowb;
-      xres = pf_rsrc(reinterpret_cast<const char*>(a.hq) + (size_t)mb * kPfTok * rowb, real ? kPfTok * rowb : 0);
-      x_sb = (uint32_t)(32 * wv) * rowb;
-    }
-    char* sb = lds + slot * kPfStageBytes;
-    const uint32_t off = (uint32_t)chunk * kPfChunk;
-#pragma unroll
-    for (int q = 0; q < kPfWInstr; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          wres, (__attribute__((address_space(3))) void*)(sb + (wv * kPfWInstr + q) * 1024), 16, w_voff,
-          w_sb + (uint32_t)(8 * q) * rowb + off, 0, kPfAux);
-#pragma unroll
-    for (int q = 0; q < kPfXInstr; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xres, (__attribute__((address_space(3))) void*)(sb + kPfWBytes + (wv * kPfXInstr + q) * 1024), 16,
-          in_cur ? cur.x_voff[q] : nxt.x_voff[q], x_sb + (uint32_t)(8 * q) * (G1 ? 0u : rowb) + off, 0,
-          kPfAux);
+    pf_issue<T, G1, WR>(a, lds, cur, nxt, cc, slot, nchunks, rowb, w_voff, wv);
   };
 
   // The empty asm makes each zero accumulator an opaque value of its own:
   // otherwise the compiler shares one zero register among all of them in the
   // first iteration and then shuffles accumulators between registers inside
   // the loop.
-  f32x4 acc[kPfTA][kPfTB];
+  f32x4 acc[L::TA][L::TB];
   auto zero_acc = [&]() {
 #pragma unroll
-    for (int i = 0; i < kPfTA; ++i)
+    for (int i = 0; i < L::TA; ++i)
 #pragma unroll
-      for (int j = 0; j < kPfTB; ++j) {
+      for (int j = 0; j < L::TB; ++j) {
         acc[i][j] = f32x4{0, 0, 0, 0};
         asm volatile("" : "+a"(acc[i][j]));
       }
@@ -360,14 +390,14 @@ __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a, int nti
   int aoff[2], boff[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    aoff[h] = pf_off(128 * wr + r16, g + 4 * h);
-    boff[h] = kPfWBytes + pf_off(64 * wc + r16, g + 4 * h);
+    aoff[h] = pf_off(L::WaveRows * wr + r16, g + 4 * h);
+    boff[h] = kPfWBytes + pf_off(L::WaveTok * wc + r16, g + 4 * h);
   }
 
   issue(0, 0);
   issue(1, 1);
   issue(2, 2);
-  pf_wait_vmcnt<2 * kPfNI>();
+  pf_wait_vmcnt<2 * L::NI>();
   pf_barrier();
 
   int q0 = 0;  // ring position of the current tile's chunk 0 (mod 3)
@@ -380,19 +410,19 @@ __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a, int nti
     //   multiply half 1 while reading half 0 of chunk c + 1 (of the next tile
     //   after the last chunk).
     // Each register set keeps one role, so the loop body is straight-line.
-    i32x4 A0[kPfTA], B0[kPfTB], A1[kPfTA], B1[kPfTB];
-    auto load_half = [&](int h, int slot, i32x4 (&A)[kPfTA], i32x4 (&B)[kPfTB]) {
+    i32x4 A0[L::TA], B0[L::TB], A1[L::TA], B1[L::TB];
+    auto load_half = [&](int h, int slot, i32x4 (&A)[L::TA], i32x4 (&B)[L::TB]) {
       const char* sb = lds + slot * kPfStageBytes;
 #pragma unroll
-      for (int j = 0; j < kPfTB; ++j) B[j] = ld16(sb + boff[h] + j * 16 * kPfChunk);
+      for (int j = 0; j < L::TB; ++j) B[j] = ld16(sb + boff[h] + j * 16 * kPfChunk);
 #pragma unroll
-      for (int i = 0; i < kPfTA; ++i) A[i] = ld16(sb + aoff[h] + i * 16 * kPfChunk);
+      for (int i = 0; i < L::TA; ++i) A[i] = ld16(sb + aoff[h] + i * 16 * kPfChunk);
     };
-    auto mult_half = [&](const i32x4 (&A)[kPfTA], const i32x4 (&B)[kPfTB]) {
+    auto mult_half = [&](const i32x4 (&A)[L::TA], const i32x4 (&B)[L::TB]) {
 #pragma unroll
-      for (int i = 0; i < kPfTA; ++i)
+      for (int i = 0; i < L::TA; ++i)
 #pragma unroll
-        for (int j = 0; j < kPfTB; ++j)
+        for (int j = 0; j < L::TB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(A[i]), as_bf16x8(B[j]), acc[i][j],
                                                               0, 0, 0);
     };
@@ -402,55 +432,55 @@ __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a, int nti
         const int slot = (q0 + c) % 3;
         load_half(1, slot, A1, B1);
         mult_half(A0, B0);
-        pf_interleave_half<kPfTA * kPfTB, false>();
-        pf_wait_vmcnt<kPfNI>();
+        pf_interleave_half<WR, L::TA * L::TB, false>();
+        pf_wait_vmcnt<L::NI>();
         pf_barrier();
         issue(c + 3, slot);
         load_half(0, slot == 2 ? 0 : slot + 1, A0, B0);
         mult_half(A1, B1);
-        pf_interleave_half<kPfTA * kPfTB, true>();
+        pf_interleave_half<WR, L::TA * L::TB, true>();
       }
-      pf_epilogue<T, G1>(a, acc, cur.fe, cur.e, cur.nt, cur.mb, wr, wc, lane);
+      pf_epilogue<T, G1, WR>(a, acc, cur.fe, cur.e, cur.nt, cur.mb, wr, wc, lane);
       task += stride;
       if (task >= end) break;
       q0 = (q0 + nchunks) % 3;
       cur = nxt;
-      nxt = pf_tile<T, G1>(a, task + stride < end ? task + stride : -1, nvalid, rowb, wv, lane);
+      nxt = pf_tile<T, G1, WR>(a, task + stride < end ? task + stride : -1, ntiles, rowb, wv, lane);
       zero_acc();
     }
   } else {
     // E4M3: one MFMA takes a whole 128-byte chunk, so whole chunks are
     // double-buffered: fragments of chunk c are read right after the barrier
     // that publishes it and multiplied one step later.
-    Raw<T> A0[kPfTA], B0[kPfTB], A1[kPfTA], B1[kPfTB];
-    auto load_frags = [&](int slot, Raw<T> (&A)[kPfTA], Raw<T> (&B)[kPfTB]) {
+    Raw<T> A0[L::TA], B0[L::TB], A1[L::TA], B1[L::TB];
+    auto load_frags = [&](int slot, Raw<T> (&A)[L::TA], Raw<T> (&B)[L::TB]) {
       const char* sb = lds + slot * kPfStageBytes;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int j = 0; j < kPfTB; ++j) B[j].q[h] = ld16(sb + boff[h] + j * 16 * kPfChunk);
+        for (int j = 0; j < L::TB; ++j) B[j].q[h] = ld16(sb + boff[h] + j * 16 * kPfChunk);
 #pragma unroll
-        for (int i = 0; i < kPfTA; ++i) A[i].q[h] = ld16(sb + aoff[h] + i * 16 * kPfChunk);
+        for (int i = 0; i < L::TA; ++i) A[i].q[h] = ld16(sb + aoff[h] + i * 16 * kPfChunk);
       }
     };
-    auto compute = [&](const Raw<T> (&A)[kPfTA], const Raw<T> (&B)[kPfTB]) {
+    auto compute = [&](const Raw<T> (&A)[L::TA], const Raw<T> (&B)[L::TB]) {
 #pragma unroll
-      for (int i = 0; i < kPfTA; ++i)
+      for (int i = 0; i < L::TA; ++i)
 #pragma unroll
-        for (int j = 0; j < kPfTB; ++j) acc[i][j] = mma(to_op<T>(A[i]), to_op<T>(B[j]), acc[i][j]);
+        for (int j = 0; j < L::TB; ++j) acc[i][j] = mma(to_op<T>(A[i]), to_op<T>(B[j]), acc[i][j]);
     };
     // Step c: wait for chunk c + 1, barrier (chunk c + 1 visible; every wave
     // holds chunk c's fragments, so its stage is free), refill that stage
     // with chunk c + 3, read chunk c + 1's fragments, multiply chunk c.
-    auto step = [&](int c, Raw<T> (&Ac)[kPfTA], Raw<T> (&Bc)[kPfTB], Raw<T> (&An)[kPfTA],
-                    Raw<T> (&Bn)[kPfTB]) {
+    auto step = [&](int c, Raw<T> (&Ac)[L::TA], Raw<T> (&Bc)[L::TB], Raw<T> (&An)[L::TA],
+                    Raw<T> (&Bn)[L::TB]) {
       const int slot = (q0 + c) % 3;
-      pf_wait_vmcnt<kPfNI>();
+      pf_wait_vmcnt<L::NI>();
       pf_barrier();
       issue(c + 3, slot);
       load_frags(slot == 2 ? 0 : slot + 1, An, Bn);
       compute(Ac, Bc);
-      pf_interleave<kPfMfma<T>()>();
+      pf_interleave<WR, L::template mfma<T>()>();
     };
     load_frags(0, A0, B0);
     while (true) {
@@ -460,12 +490,12 @@ __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(GemmArgs a, int nti
         step(c + 1, A1, B1, A0, B0);
       }
       if (c < nchunks) step(c, A0, B0, A1, B1);  // odd count: one tile per workgroup only
-      pf_epilogue<T, G1>(a, acc, cur.fe, cur.e, cur.nt, cur.mb, wr, wc, lane);
+      pf_epilogue<T, G1, WR>(a, acc, cur.fe, cur.e, cur.nt, cur.mb, wr, wc, lane);
       task += stride;
       if (task >= end) break;
       q0 = (q0 + nchunks) % 3;
       cur = nxt;
-      nxt = pf_tile<T, G1>(a, task + stride < end ? task + stride : -1, nvalid, rowb, wv, lane);
+      nxt = pf_tile<T, G1, WR>(a, task + stride < end ? task + stride : -1, ntiles, rowb, wv, lane);
       zero_acc();
     }
   }
@@ -503,11 +533,21 @@ static int pf_persistent_grid(long long tiles) {
   return (int)(g / 8 * 8);
 }
 
+// Wave layout per operand type and product (measured on MI355X at T = 4096
+// and 8192): 8 waves of 64 x 64 for bf16 and the E4M3 down product, 4 waves of
+// 128 x 64 for the E4M3 gate/up product.
+template <int T, bool G1>
+constexpr int pf_wr() {
+  return (T == DT_E4M3 && G1) ? 2 : 4;
+}
+
 template <int T, bool G1>
 static int pf_launch(const GemmArgs& a, hipStream_t st) {
+  constexpr int WR = pf_wr<T, G1>();
+  using L = PfL<WR>;
   static bool attr_set = false;  // per process: one device's attribute covers the kernel
   if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&pf_gemm_kernel<T, G1>),
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&pf_gemm_kernel<T, G1, WR>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, kPfLdsBytes);
     if (err != hipSuccess) return (int)err;
     attr_set = true;
@@ -519,10 +559,10 @@ static int pf_launch(const GemmArgs& a, hipStream_t st) {
   const long long tasks = (long long)ntiles * a.max_blocks;  // block_m >= 128: 128-row tiles
   const int pgrid = persist ? pf_persistent_grid(tasks) : 0;
   if (pgrid > 0) {
-    hipLaunchKernelGGL((pf_gemm_kernel<T, G1>), dim3(pgrid), dim3(kPfThreads), kPfLdsBytes, st, a, ntiles, 1);
+    hipLaunchKernelGGL((pf_gemm_kernel<T, G1, WR>), dim3(pgrid), dim3(L::Threads), kPfLdsBytes, st, a, ntiles, 1);
   } else {
     dim3 grid(ntiles, a.max_blocks);
-    hipLaunchKernelGGL((pf_gemm_kernel<T, G1>), grid, dim3(kPfThreads), kPfLdsBytes, st, a, ntiles, 0);
+    hipLaunchKernelGGL((pf_gemm_kernel<T, G1, WR>), grid, dim3(L::Threads), kPfLdsBytes, st, a, ntiles, 0);
   }
   return (int)hipGetLastError();
 }
