@@ -25,7 +25,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 2500.0, "e4m3": 5000.0}
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 KERNEL_SRCS = [os.path.join(ROOT, "mixture_experts_layer_13_amd", "csrc", f)
-               for f in ("gemm.hip", "ring.hip", "prefill.hip", "common.hpp")]
+               for f in ("gemm.hip", "ring.hip", "prefill.hip", "prefill2.hip", "common.hpp")]
 
 
 def kernel_source_sha():
@@ -172,8 +172,10 @@ def main():
     ring = stream_path and wl.w_dtype in ("bf16", "e4m3") and (H * bw) % 512 == 0 and H * bw >= 2048
     if stream_path:
         roof["kernel"] = "gemm1_ring_kernel" if ring else "gemm1_stream_kernel"
-    else:  # block_m 128 (the layer's choice above 64 tokens): the prefill kernel
-        roof["kernel"] = "pf_gemm_kernel" if wl.w_dtype in ("bf16", "e4m3") else "gemm1_tile_kernel"
+    elif wl.w_dtype in ("bf16", "e4m3"):  # prefill kernels: 256 x 256 tiles with 256-row blocks
+        roof["kernel"] = "pfq_gemm_kernel" if layer.block_m == 256 else "pf_gemm_kernel"
+    else:
+        roof["kernel"] = "gemm1_tile_kernel"
     roof["avg_launch_us"] = round(g1_ms * 1e3, 2)
     roof["algorithmic_bytes_per_launch"] = int(g1_bytes)
     if os.path.exists(PMC_FILE):
@@ -235,7 +237,8 @@ def main():
         "data": "synthetic (seeded; no public dataset or trained weights on the pages)",
         "config": {"workload": f"{args.workload} T={T} H={H} I={I} E={E} top-{k}",
                    "tokens": T, "hidden": H, "intermediate": I, "experts": E, "topk": k,
-                   "active_experts": U, "kernel_family": "stream" if stream_path else "tile"},
+                   "active_experts": U, "block_m": layer.block_m,
+                   "kernel_family": "stream" if stream_path else "tile"},
         "op_hbm_gbps": round(op_bytes / (ms_step * 1e-3) / 1e9, 1),
         "op_tflops": round(flops / (ms_step * 1e-3) / 1e12, 3),
         "down_gemm_avg_launch_us": round(g2_ms * 1e3, 2),

@@ -32,12 +32,21 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
 }
 
-// binary32 -> bfloat16, round to nearest even (NaN kept quiet).
+// binary32 -> bfloat16, round to nearest even (NaN kept quiet); written
+// without a branch so that it stays a few selects in unrolled epilogues.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return (u & 0x7fffffffu) > 0x7f800000u ? ((u >> 16) | 0x40u) : rounded;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two binary32 values -> packed bfloat16 pair (a in the low half), round to
+// nearest even: one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
 }
 
 // binary32 -> OCP E4M3FN code: round to nearest even, saturate to +-448,
@@ -243,6 +252,13 @@ __device__ __forceinline__ f32x4 mma(const OpF8& a, const OpF8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.v, b.v, c, 0, 0, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// SiLU(z) = z / (1 + e^-z) with the hardware base-2 exponential and
+// reciprocal (each within about 1 ulp), so a few ulps from the rounded fp32
+// value: z * rcp(1 + 2^(-z log2 e)).  Large negative z gives 2^(+big) = inf
+// and z * rcp(inf) = -0, the limit.
+__device__ __forceinline__ float silu(float z) {
+  const float e = __builtin_amdgcn_exp2f(-z * 1.44269504088896340736f);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 }  // namespace moe

@@ -214,8 +214,8 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(GemmArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) hmax = fmaxf(hmax, __builtin_fabsf(h[i]));
         } else {
-          uint2 pk = make_uint2(f32_to_bf16_bits(h[0]) | (f32_to_bf16_bits(h[1]) << 16),
-                                f32_to_bf16_bits(h[2]) | (f32_to_bf16_bits(h[3]) << 16));
+          uint2 pk = make_uint2(pack_bf16x2(h[0], h[1]),
+                                pack_bf16x2(h[2], h[3]));
           *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.h) + idx) = pk;
         }
       }
@@ -377,8 +377,8 @@ __device__ __forceinline__ void store_out4<DT_F32>(void* out, size_t idx, const 
 template <>
 __device__ __forceinline__ void store_out4<DT_BF16>(void* out, size_t idx, const float v[4]) {
   *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + idx) =
-      make_uint2(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
-                 f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
+      make_uint2(pack_bf16x2(v[0], v[1]),
+                 pack_bf16x2(v[2], v[3]));
 }
 
 // ================================================================== tile
@@ -553,8 +553,8 @@ __global__ __launch_bounds__(256) void gemm1_tile_kernel(GemmArgs a) {
         for (int i = 0; i < 4; ++i) hmax = fmaxf(hmax, __builtin_fabsf(h[i]));
       } else {
         *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.h) + idx) =
-            make_uint2(f32_to_bf16_bits(h[0]) | (f32_to_bf16_bits(h[1]) << 16),
-                       f32_to_bf16_bits(h[2]) | (f32_to_bf16_bits(h[3]) << 16));
+            make_uint2(pack_bf16x2(h[0], h[1]),
+                       pack_bf16x2(h[2], h[3]));
       }
     }
   }
@@ -734,6 +734,7 @@ static int g1t_dispatch(const GemmArgs& a, hipStream_t st) {
 }
 
 int launch_gemm1_tile(const GemmArgs& a, hipStream_t st) {
+  if (pfq_applies(a, true)) return launch_gemm1_pfq(a, st);
   if (pf_applies(a, true)) return launch_gemm1_prefill(a, st);
   // tile operands: bf16 family needs bf16 activations (f32 ones are cast first)
   if (a.wt == DT_E4M3) return g1t_dispatch<DT_E4M3, DT_E4M3>(a, st);
@@ -758,6 +759,7 @@ static int g2t_dispatch(const GemmArgs& a, hipStream_t st) {
 }
 
 int launch_gemm2_tile(const GemmArgs& a, hipStream_t st) {
+  if (pfq_applies(a, false)) return launch_gemm2_pfq(a, st);
   if (pf_applies(a, false)) return launch_gemm2_prefill(a, st);
   if (a.wt == DT_E4M3) return g2t_dispatch<DT_E4M3>(a, st);
   if (a.wt == DT_BF16) return g2t_dispatch<DT_BF16>(a, st);

@@ -82,6 +82,9 @@ int launch_gemm2_ring(const GemmArgs& a, hipStream_t stream);
 bool pf_applies(const GemmArgs& a, bool gemm1);
 int launch_gemm1_prefill(const GemmArgs& a, hipStream_t stream);
 int launch_gemm2_prefill(const GemmArgs& a, hipStream_t stream);
+bool pfq_applies(const GemmArgs& a, bool gemm1);
+int launch_gemm1_pfq(const GemmArgs& a, hipStream_t stream);
+int launch_gemm2_pfq(const GemmArgs& a, hipStream_t stream);
 int launch_gemm1_tile(const GemmArgs& a, hipStream_t stream);
 int launch_gemm2_tile(const GemmArgs& a, hipStream_t stream);
 int launch_combine(const GemmArgs& a, hipStream_t stream);

@@ -183,8 +183,8 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a,
             for (int t = 0; t < 4; ++t) hmax = fmaxf(hmax, __builtin_fabsf(h[t]));
           } else {
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.h) + idx) =
-                make_uint2(f32_to_bf16_bits(h[0]) | (f32_to_bf16_bits(h[1]) << 16),
-                           f32_to_bf16_bits(h[2]) | (f32_to_bf16_bits(h[3]) << 16));
+                make_uint2(pack_bf16x2(h[0], h[1]),
+                           pack_bf16x2(h[2], h[3]));
           }
         }
       }
@@ -210,8 +210,8 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a,
                               acc[i][j][3] * scale};
           if (ybf)
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + idx) =
-                make_uint2(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
-                           f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
+                make_uint2(pack_bf16x2(v[0], v[1]),
+                           pack_bf16x2(v[2], v[3]));
           else
             st16(reinterpret_cast<float*>(a.y) + idx,
                  i32x4{__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3])});

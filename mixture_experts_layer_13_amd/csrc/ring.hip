@@ -240,8 +240,8 @@ __global__ __launch_bounds__(256) void gemm1_ring_kernel(GemmArgs a) {
           for (int i = 0; i < 4; ++i) hmax = fmaxf(hmax, __builtin_fabsf(h[i]));
         } else {
           *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.h) + idx) =
-              make_uint2(f32_to_bf16_bits(h[0]) | (f32_to_bf16_bits(h[1]) << 16),
-                         f32_to_bf16_bits(h[2]) | (f32_to_bf16_bits(h[3]) << 16));
+              make_uint2(pack_bf16x2(h[0], h[1]),
+                         pack_bf16x2(h[2], h[3]));
         }
       }
     }
@@ -559,8 +559,8 @@ __global__ __launch_bounds__(512) void gemm2_ring_kernel(GemmArgs a, int maxU, i
     }
     if (OT == DT_BF16) {
       *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + (size_t)t * K + n0 + q) =
-          make_uint2(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
-                     f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
+          make_uint2(pack_bf16x2(v[0], v[1]),
+                     pack_bf16x2(v[2], v[3]));
     } else {
       st16(reinterpret_cast<float*>(a.out) + (size_t)t * K + n0 + q,
            i32x4{__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]),

@@ -217,7 +217,10 @@ class FusedMoE:
                  block_m=None, a_dtype=torch.bfloat16, out_dtype=torch.bfloat16,
                  renormalize=True, a1_scale=None, a2_scale=None, device="cuda"):
         if block_m is None:
-            block_m = 16 if M <= 64 else 128
+            # alignment block: 16 rows for decode-sized batches (the stream and
+            # ring kernels), 256 once the experts average 512 rows or more (the
+            # 256 x 256 prefill tiles), else 128
+            block_m = 16 if M <= 64 else (256 if M * topk >= 512 * E else 128)
         self.M, self.K, self.N, self.E, self.topk = M, K, N, E, topk
         self.block_m, self.renormalize = block_m, renormalize
         self.w13, self.w2, self.w13_scale, self.w2_scale = w13, w2, w13_scale, w2_scale

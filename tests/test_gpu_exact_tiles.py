@@ -53,8 +53,10 @@ GATE_UP = [
     (0, torch.bfloat16, 40, 2048, 256, 8, 2, 16),    # ring, two column blocks
     (0, torch.float8_e4m3fn, 40, 2048, 256, 8, 2, 16),
     (0, torch.float32, 12, 512, 256, 8, 2, 16),      # stream kernel (f32 weights)
-    (1, torch.bfloat16, 200, 1024, 256, 8, 2, 128),  # prefill kernel
-    (1, torch.float8_e4m3fn, 200, 1024, 256, 8, 2, 256),
+    (1, torch.bfloat16, 200, 1024, 256, 8, 2, 128),  # prefill kernel, 256 x 128 tiles
+    (1, torch.float8_e4m3fn, 200, 1024, 256, 8, 2, 256),  # 256 x 256 tiles
+    (1, torch.bfloat16, 300, 1024, 256, 8, 2, 256),
+    (1, torch.float8_e4m3fn, 300, 2048, 512, 8, 2, 128),
     (1, torch.bfloat16, 150, 512, 256, 8, 2, 32),    # tile kernel, 32-row blocks
 ]
 
@@ -85,8 +87,10 @@ DOWN = [
     (0, torch.bfloat16, 5, 2048, 512, 8, 2, 16),     # ring down kernel (4 <= M <= 16)
     (0, torch.bfloat16, 40, 2048, 512, 8, 2, 16),    # stream down kernel
     (0, torch.float8_e4m3fn, 12, 2048, 1024, 8, 2, 16),
-    (1, torch.bfloat16, 200, 2048, 512, 8, 2, 128),  # prefill kernel + combine
+    (1, torch.bfloat16, 200, 2048, 512, 8, 2, 128),  # prefill kernel + combine, 256 x 128
     (1, torch.float8_e4m3fn, 200, 2048, 512, 8, 2, 128),
+    (1, torch.bfloat16, 300, 2048, 512, 8, 2, 256),  # 256 x 256 tiles
+    (1, torch.float8_e4m3fn, 300, 2048, 1024, 8, 2, 256),
     (1, torch.bfloat16, 150, 1024, 256, 8, 2, 64),   # tile kernel + combine
 ]
 

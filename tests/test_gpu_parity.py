@@ -209,6 +209,9 @@ PREFILL_SMALL = [
     ("bf16_T600_persist", "decode_bf16", 600, 1024, 512, 8, 4, 128),
     ("fp8_T600_persist", "decode_fp8", 600, 1024, 512, 8, 4, 128),
     ("fp8_T700_persist_bm256", "large_fp8", 700, 1024, 512, 16, 4, 256),
+    # 256 x 256 tiles (256-row blocks) for both products, bf16 and E4M3
+    ("bf16_T900_bm256", "decode_bf16", 900, 1024, 512, 8, 4, 256),
+    ("fp8_T900_bm256", "decode_fp8", 900, 1024, 1024, 8, 4, 256),
 ]
 
 
