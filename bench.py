@@ -44,8 +44,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_bf16")
     ap.add_argument("--tokens", type=int, default=64)
-    ap.add_argument("--cpu-sample", type=int, default=16,
+    ap.add_argument("--cpu-sample", type=int, default=64,
                     help="tokens of the batch the CPU oracle is timed on (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="host seconds the oracle timing aims at (repeats of the sample)")
     ap.add_argument("--copy-check", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -190,8 +192,10 @@ def main():
     if args.cpu_sample > 0:
         import oracle
 
+        # the oracle on the first S tokens of the same batch, repeated until
+        # about --cpu-seconds of host work have been timed (one untimed pass
+        # first, which also sizes the repeat count)
         S = min(args.cpu_sample, T)
-        tok = np.arange(S)
         lg = logits.cpu().numpy()
         rids, rw = oracle.route_topk(lg, k, True)
         used = np.unique(rids[:S])
@@ -205,22 +209,29 @@ def main():
             s13 = d["w13_scale"].index_select(0, sel).cpu().numpy()
             s2 = d["w2_scale"].index_select(0, sel).cpu().numpy()
         xb = inputs.to_numpy_bits(x)
+
+        def oracle_pass():
+            ro = oracle.route_topk(lg[:S], k, True)  # routing of the sample, timed
+            return oracle.moe_forward(xb[:S], w13, w2, remap[ro[0]], ro[1], s13, s2, fp8_act=fp8,
+                                      a2_scale=(0.05 if fp8 else None))[0]
+
         c0 = time.perf_counter()
-        ro = oracle.route_topk(lg[:S], k, True)  # routing of the sample, timed
-        rids_s = remap[ro[0]]
-        ref, _ = oracle.moe_forward(xb[:S], w13, w2, rids_s, ro[1], s13, s2, fp8_act=fp8,
-                                    a2_scale=(0.05 if fp8 else None))
-        c1 = time.perf_counter()
-        got = out_rows = layer.out[:S].float().cpu().numpy().astype(np.float64)
+        ref = oracle_pass()
+        once = time.perf_counter() - c0
+        reps = max(1, int(np.ceil(args.cpu_seconds / max(once, 1e-3))))
+        c0 = time.perf_counter()
+        for _ in range(reps):
+            oracle_pass()
+        wall = time.perf_counter() - c0
+        got = layer.out[:S].float().cpu().numpy().astype(np.float64)
         cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
-        cpu = {"value": round(S / (c1 - c0), 3), "unit": "tokens/s", "cores": cores,
+        cpu = {"value": round(S * reps / wall, 3), "unit": "tokens/s", "cores": cores,
                "kind": "oracle",
-               "sample": f"first {S} tokens of the same batch (routing + {S}x{k} expert "
-                         f"pairs in fp64), {c1 - c0:.2f} s wall"}
+               "sample": f"first {S} tokens of the same batch (routing + {S}x{k} expert pairs in "
+                         f"fp64), {reps} passes, {wall:.1f} s wall"}
         if not fp8:
             err = float((np.abs(got - ref).max(1) / np.abs(ref).max(1)).max())
             cpu["sample_max_row_rel_err_vs_gpu"] = float(f"{err:.3e}")
-        del out_rows
 
     line = {
         "metric": "fused-MoE tokens/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)",
