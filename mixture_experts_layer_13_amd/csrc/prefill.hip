@@ -394,8 +394,14 @@ __global__ __launch_bounds__(PfL<WR>::Threads) void pf_gemm_kernel(GemmArgs a, i
     boff[h] = kPfWBytes + pf_off(L::WaveTok * wc + r16, g + 4 * h);
   }
 
+  // chunks 0, 1, 2 in this order (the wait counts chunks 1 and 2 as the
+  // loads still allowed in flight), so the scheduler may not interleave them
   issue(0, 0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   issue(1, 1);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   issue(2, 2);
   pf_wait_vmcnt<2 * L::NI>();
   pf_barrier();

@@ -579,6 +579,10 @@ __global__ __launch_bounds__(NW * 64) void pfq_gemm_kernel(GemmArgs a, int ntile
   {
     const QDma<NW> d0 = q_plan<G1, NW>(a, cur, 0, stage0, rowb, wv);
     q_dmas<NW, 0, 2 * L::Instr>(d0, wvoff, wv);
+    // chunk 1's DMA must not be scheduled above chunk 0's: the wait below
+    // counts chunk 1 as the only loads still allowed in flight
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     const QDma<NW> d1 = q_plan<G1, NW>(a, cur, 1, stage1, rowb, wv);
     q_dmas<NW, 0, 2 * L::Instr>(d1, wvoff, wv);
   }

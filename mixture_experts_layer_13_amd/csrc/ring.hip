@@ -51,6 +51,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
   asm volatile("" ::: "memory");
 }
+// Keeps one ring stage's loads (register x/h fragments and LDS DMA) in
+// program order relative to the next stage's.  The hand-counted vmcnt waits
+// assume every stage's instructions were issued before any of a later
+// stage's; without a fence the scheduler may hoist a later stage's DMA above
+// an earlier stage's register loads (which wait for the token ids), and a
+// wait for "all but the last (D-1) stages" then leaves part of the stage
+// being read still in flight.
+__device__ __forceinline__ void stage_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 // Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -69,28 +80,37 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int WT, int NCB>
+// NRB row blocks per workgroup (16 gate + 16 up rows each) go through the
+// ring one after the other: stage p < ns is row block 0's K stage p, stage
+// ns + k row block 1's stage k.  More stages per workgroup amortise the
+// ring's fill and drain (for E4M3 a row block alone is only 8 stages).
+template <int WT, int NCB, int NRB>
 struct G1Ring {
   static constexpr int D = kRingD;
   static constexpr int SB = 128;              // bytes per K-step of a row (both families)
   static constexpr int NI = 4 + 2 * NCB;      // vector-memory instructions per issue
   char* lds;
-  const char* src[4];   // this lane's DMA source per block (stage 0)
+  const char* src[4];   // this lane's DMA source per block (stage 0, row block 0)
   int dst[4];           // LDS offset of each of this wave's blocks
   const char* xr[NCB];  // this lane's x row (+ lane-group offset)
   Raw<WT> xs[D][NCB];
   int wv;
+  int ns;               // stages of one row block
+  size_t rbstride;      // bytes from one row block's rows to the next one's
 
   template <int SLOT>
   __device__ __forceinline__ void issue(int p) {
+    const int rb = (NRB > 1 && p >= ns) ? 1 : 0;
+    const int k = p - rb * ns;  // K stage within the row block
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
-      xs[SLOT][cb] = load_raw<WT>(xr[cb] + (size_t)(p * 4 + wv) * SB);
+      xs[SLOT][cb] = load_raw<WT>(xr[cb] + (size_t)(k * 4 + wv) * SB);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(src[q] + (size_t)p * kRingRowBytes),
+          reinterpret_cast<const void*>(src[q] + rb * rbstride + (size_t)k * kRingRowBytes),
           reinterpret_cast<void*>(lds + SLOT * kG1StageBytes + dst[q]), 16, 0, kRingAux);
+    stage_fence();
   }
 
   // One stage: ISSUE = 1 refills the ring with stage st + D - 1 first (steady
@@ -128,8 +148,8 @@ struct G1Ring {
   }
 };
 
-template <int WT, int NCB>
-__global__ __launch_bounds__(256) void gemm1_ring_kernel(GemmArgs a) {
+template <int WT, int NCB, int NRB>
+__global__ __launch_bounds__(256, 2) void gemm1_ring_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   constexpr int D = kRingD;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -139,14 +159,16 @@ __global__ __launch_bounds__(256) void gemm1_ring_kernel(GemmArgs a) {
   if (e < 0) return;  // uniform over the workgroup
   const int seg0 = a.offsets[e], seg1 = a.offsets[e + 1];
   const int me = segment_count(a.sorted_ids, seg0, seg1, a.P);
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * 16 * NRB;
   const int K = a.K, N = a.N;
   constexpr int WB = Family<WT>::kBytes;
   const int ns = K * WB / kRingRowBytes;
 
-  G1Ring<WT, NCB> R;
+  G1Ring<WT, NCB, NRB> R;
   R.lds = lds;
   R.wv = wv;
+  R.ns = ns;
+  R.rbstride = (size_t)16 * K * WB;
   const char* w13 = reinterpret_cast<const char*>(a.w13);
   {
     const int lrow = lane >> 5;
@@ -175,42 +197,56 @@ __global__ __launch_bounds__(256) void gemm1_ring_kernel(GemmArgs a) {
       const int f = a.sorted_ids[seg0 + (col < me ? col : 0)];
       R.xr[cb] = xb + (size_t)(f / a.topk) * K * WB;
     }
-    f32x4 accg[NCB], accu[NCB];
+    f32x4 accg[NRB][NCB], accu[NRB][NCB];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) accg[cb] = accu[cb] = f32x4{0, 0, 0, 0};
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) accg[rb][cb] = accu[rb][cb] = f32x4{0, 0, 0, 0};
+    // stage s of the sequence: slot SL, refill (IS) or drain; row block 1's
+    // stages accumulate into its own registers
+    auto stage = [&](auto slot, auto is, int s) {
+      constexpr int SL = decltype(slot)::value;
+      constexpr bool IS = decltype(is)::value;
+      if (NRB == 1 || s < ns)
+        R.template body<SL, IS>(s, ncb, r16, g, accg[0], accu[0]);
+      else
+        R.template body<SL, IS>(s, ncb, r16, g, accg[NRB - 1], accu[NRB - 1]);
+    };
+    using Refill = std::true_type;
+    using Drain = std::false_type;
+    const int total = NRB * ns;
 
     // prologue: stages 0 .. D - 2
     static_for<0, D - 1>([&](auto i) { R.template issue<decltype(i)::value>(decltype(i)::value); });
-    // steady state: whole trips of D stages that all refill (ns >= D)
-    const int n_issue = ns - (D - 1);  // stages that refill the ring
+    // steady state: whole trips of D stages that all refill (total >= D)
+    const int n_issue = total - (D - 1);  // stages that refill the ring
     int st = 0;
     for (; st + D <= n_issue; st += D)
-      static_for<0, D>([&](auto i) {
-        R.template body<decltype(i)::value, true>(st + decltype(i)::value, ncb, r16, g, accg, accu);
-      });
+      static_for<0, D>([&](auto i) { stage(i, Refill{}, st + decltype(i)::value); });
     // the last n_issue % D refilling stages, then D - 1 draining ones; slot =
     // stage % D is static in every branch
     const int rem = n_issue - st;  // 0 .. D - 1
     static_for<0, D>([&](auto rr) {
       constexpr int RR = decltype(rr)::value;
       if (rem == RR) {
-        static_for<0, RR>([&](auto i) {
-          R.template body<decltype(i)::value, true>(st + decltype(i)::value, ncb, r16, g, accg, accu);
-        });
+        static_for<0, RR>([&](auto i) { stage(i, Refill{}, st + decltype(i)::value); });
         static_for<0, D - 1>([&](auto j) {
           constexpr int J = decltype(j)::value;
-          R.template body<(RR + J) % D, false>(st + RR + J, ncb, r16, g, accg, accu);
+          stage(std::integral_constant<int, (RR + J) % D>{}, Drain{}, st + RR + J);
         });
       }
     });
 
-    // reduce the 4 K-slices (the ring is drained: every body ended with a barrier)
+    // reduce the 4 K-slices of each row block (the ring is drained: every
+    // body ended with a barrier)
+    static_for<0, NRB>([&](auto rbc) {
+    constexpr int RB = decltype(rbc)::value;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        red[((((wv * 2 + 0) * NCB + cb) * 4 + i) << 6) + lane] = accg[cb][i];
-        red[((((wv * 2 + 1) * NCB + cb) * 4 + i) << 6) + lane] = accu[cb][i];
+        red[((((wv * 2 + 0) * NCB + cb) * 4 + i) << 6) + lane] = accg[RB][cb][i];
+        red[((((wv * 2 + 1) * NCB + cb) * 4 + i) << 6) + lane] = accu[RB][cb][i];
       }
     __syncthreads();
     for (int cb = wv; cb < ncb; cb += 4) {
@@ -229,9 +265,9 @@ __global__ __launch_bounds__(256) void gemm1_ring_kernel(GemmArgs a) {
         h[i] = silu(g4[i]) * u4[i];
       }
       if (a.probe) {
-        if (col < me) probe_store(a, (size_t)(seg0 + col), n0 + 4 * g, g4, u4);
+        if (col < me) probe_store(a, (size_t)(seg0 + col), n0 + 16 * RB + 4 * g, g4, u4);
       } else if (col < me) {
-        const size_t idx = (size_t)(seg0 + col) * N + n0 + 4 * g;
+        const size_t idx = (size_t)(seg0 + col) * N + n0 + 16 * RB + 4 * g;
         if (WT == DT_E4M3) {
           st16(reinterpret_cast<float*>(a.h) + idx,
                i32x4{__float_as_int(h[0]), __float_as_int(h[1]), __float_as_int(h[2]),
@@ -245,7 +281,8 @@ __global__ __launch_bounds__(256) void gemm1_ring_kernel(GemmArgs a) {
         }
       }
     }
-    __syncthreads();  // red aliases the ring: drain before the next pass refills it
+    __syncthreads();  // red aliases the ring: drain before it is reused
+    });
   }
   if (WT == DT_E4M3) {
     hmax = wave_max(hmax);
@@ -260,28 +297,39 @@ bool gemm1_ring_applies(const GemmArgs& a) {
   return row % kRingRowBytes == 0 && row / kRingRowBytes >= kRingD;
 }
 
-template <int WT, int NCB>
+template <int WT, int NCB, int NRB>
 static int g1r_launch(const GemmArgs& a, hipStream_t st) {
   const size_t ring = (size_t)kRingD * kG1StageBytes;
   const size_t red = (size_t)4 * 2 * NCB * 4 * kWave * sizeof(float);
   const size_t lds = ring > red ? ring : red;
   static bool attr = false;
   if (!attr) {
-    int err = (int)hipFuncSetAttribute((const void*)gemm1_ring_kernel<WT, NCB>,
+    int err = (int)hipFuncSetAttribute((const void*)gemm1_ring_kernel<WT, NCB, NRB>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err) return err;
     attr = true;
   }
-  dim3 grid(a.N / 16, min(a.E, a.P));
-  hipLaunchKernelGGL((gemm1_ring_kernel<WT, NCB>), grid, dim3(256), lds, st, a);
+  dim3 grid(a.N / (16 * NRB), min(a.E, a.P));
+  hipLaunchKernelGGL((gemm1_ring_kernel<WT, NCB, NRB>), grid, dim3(256), lds, st, a);
   return (int)hipGetLastError();
+}
+
+// Two row blocks per workgroup for E4M3 with one token column block (half
+// the bytes per row, so one row block is too short a stream; measured 5-7%
+// faster at T = 1-16).  With two column blocks the second row block's
+// accumulators no longer fit two workgroups per CU without spilling, which
+// costs more than it gains, so bf16 and wider batches keep one.
+template <int WT>
+static int g1r_dispatch(const GemmArgs& a, hipStream_t st, int ncb) {
+  if constexpr (WT == DT_E4M3) {
+    if (ncb <= 1 && a.N % 32 == 0) return g1r_launch<WT, 1, 2>(a, st);
+  }
+  return ncb <= 1 ? g1r_launch<WT, 1, 1>(a, st) : g1r_launch<WT, 2, 1>(a, st);
 }
 
 int launch_gemm1_ring(const GemmArgs& a, hipStream_t st) {
   const int ncb = min((min(a.M, kStreamMaxM) + 15) / 16, kRingNcbMax);
-  if (a.wt == DT_E4M3)
-    return ncb <= 1 ? g1r_launch<DT_E4M3, 1>(a, st) : g1r_launch<DT_E4M3, 2>(a, st);
-  return ncb <= 1 ? g1r_launch<DT_BF16, 1>(a, st) : g1r_launch<DT_BF16, 2>(a, st);
+  return a.wt == DT_E4M3 ? g1r_dispatch<DT_E4M3>(a, st, ncb) : g1r_dispatch<DT_BF16>(a, st, ncb);
 }
 
 }  // namespace moe
@@ -499,6 +547,7 @@ __global__ __launch_bounds__(512) void gemm2_ring_kernel(GemmArgs a, int maxU, i
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) hs[SLOT][cb] = load_raw<HT>(h_src(ci, cb));
     issue_dma(ci, SLOT);
+    stage_fence();
     advance(ci);
     ++issued;
   };
