@@ -672,6 +672,18 @@ __global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict_
 
 // ------------------------------------------------------------------ launch
 
+int device_cu_count() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus = n;
+  }
+  return cus;
+}
+
 template <int WT, int XT>
 static int g1s_dispatch(const GemmArgs& a, hipStream_t st, dim3 grid) {
   const int ncb = min((min(a.M, kStreamMaxM) + 15) / 16, kStreamMaxNcb);

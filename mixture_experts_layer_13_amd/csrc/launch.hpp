@@ -90,6 +90,9 @@ int launch_gemm2_tile(const GemmArgs& a, hipStream_t stream);
 int launch_combine(const GemmArgs& a, hipStream_t stream);
 int launch_cast_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t stream);
 
+// Compute units of the current device (queried once).
+int device_cu_count();
+
 // Largest M served by the streaming (decode) kernels.
 constexpr int kStreamMaxM = 64;
 

@@ -17,11 +17,11 @@
 // stay lane-ordered), which puts the 16 rows one ds_read_b128 touches on 16
 // different bank groups.
 //
-// Workgroup: 4 waves, 16 gate + 16 up rows of one active expert; every stage
-// is 512 bytes of each of the 32 rows (4 K-steps), one step per wave.  Each
-// wave keeps its own x fragments of the kRingD - 1 stages in flight in
-// registers, issued together with the stage's DMA so that a single in-order
-// vmcnt wait covers both.
+// Gate/up stage: 512 bytes of each of 32 rows (16 gate + 16 up rows of one
+// expert, 4 K-steps), one step per wave of a 4-wave workgroup.  Each wave
+// keeps its own x fragments of the kRingD - 1 stages in flight in registers,
+// issued together with the stage's DMA so that a single in-order vmcnt wait
+// covers both.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -80,53 +80,99 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// NRB row blocks per workgroup (16 gate + 16 up rows each) go through the
-// ring one after the other: stage p < ns is row block 0's K stage p, stage
-// ns + k row block 1's stage k.  More stages per workgroup amortise the
-// ring's fill and drain (for E4M3 a row block alone is only 8 stages).
-template <int WT, int NCB, int NRB>
-struct G1Ring {
-  static constexpr int D = kRingD;
-  static constexpr int SB = 128;              // bytes per K-step of a row (both families)
-  static constexpr int NI = 4 + 2 * NCB;      // vector-memory instructions per issue
-  char* lds;
-  const char* src[4];   // this lane's DMA source per block (stage 0, row block 0)
-  int dst[4];           // LDS offset of each of this wave's blocks
-  const char* xr[NCB];  // this lane's x row (+ lane-group offset)
-  Raw<WT> xs[D][NCB];
-  int wv;
-  int ns;               // stages of one row block
-  size_t rbstride;      // bytes from one row block's rows to the next one's
+// ------------------------------------------------------------ gate/up ring
+//
+// One launch of a fixed number of workgroups (WPC per CU) that walk a static
+// list of tasks without draining the ring between them.  Task = (column group, 16-row block): a column group
+// is 16*NCB consecutive positions of one alignment block (block_m = 16*NCB, or
+// a multiple of it, then one block is several groups), and a row block is
+// gate rows n0..n0+15 with the matching up rows, of the block's expert.  Tasks
+// are numbered group-major; workgroup w takes tasks w, w + G, w + 2G, ... (G
+// workgroups), so every workgroup streams the same number of weight bytes (to
+// one task), the ring fills and drains once per workgroup instead of once per
+// row block, and at any moment the workgroups read neighbouring tasks (the
+// order a one-task-per-workgroup launch would dispatch them in).  Everything a
+// task needs before its first load -- expert, dequant scale, row block, the
+// token row of each column -- is read into an LDS table row when the
+// workgroup starts, so that switching tasks inside the stream reads only LDS
+// and never waits on the vector-memory counter the ring runs on.
+//
+// At the end of a task the four K-slices are summed by wave 0 (waves 1..3
+// leave their partial sums in a small LDS area beside the ring) while the
+// other waves already work on the next task's stages.
 
-  template <int SLOT>
-  __device__ __forceinline__ void issue(int p) {
-    const int rb = (NRB > 1 && p >= ns) ? 1 : 0;
-    const int k = p - rb * ns;  // K stage within the row block
+constexpr int kPRedBytesPerCb = 3 * 2 * 4 * kWave * 4;  // waves 1..3 x gate/up x 4 regs x lanes
+
+template <int WT, int NCB, int D>
+struct PRing {
+  static constexpr int SB = 128;          // bytes per K-step of a row
+  static constexpr int NI = 4 + 2 * NCB;  // vector-memory instructions per issue
+  static constexpr int WB = Family<WT>::kBytes;
+  static constexpr int CPG = 16 * NCB;    // columns per group
+  // table row: expert, scale bits, row block, first sorted position, K stage
+  // the task starts at, then the token row of every column (-1: padding)
+  static constexpr int TW = CPG + 5;
+  char* ring;
+  float* red;
+  const int* tab;
+  const char* w13;
+  const char* xb;  // x + this lane's 32-byte offset within a K-step
+  int K, N, ns, wv, r16, lrow, lb, ng;
+  // issue cursor: table row (task of this workgroup), stage within the task
+  int iq, ik;
+  int irot;  // K stage the task starts at (tasks walk K from different offsets)
+  const char* src[4];
+  const char* xr[NCB];
+  int dst[4];
+  Raw<WT> xs[D][NCB];
+
+  __device__ __forceinline__ void set_task(int q) {
+    const int* row = tab + q * TW;
+    const int e = row[0], rb = row[2];
+    const int n0 = rb * 16;
+    irot = row[4];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-      xs[SLOT][cb] = load_raw<WT>(xr[cb] + (size_t)(k * 4 + wv) * SB);
+    for (int qq = 0; qq < 4; ++qq) {
+      const int r = 2 * (4 * wv + qq) + lrow;
+      const int grow = (r < 16) ? (n0 + r) : (N + n0 + r - 16);
+      src[qq] = w13 + ((size_t)e * 2 * N + grow) * K * WB + lb;
+    }
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(src[q] + rb * rbstride + (size_t)k * kRingRowBytes),
-          reinterpret_cast<void*>(lds + SLOT * kG1StageBytes + dst[q]), 16, 0, kRingAux);
-    stage_fence();
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int t = row[5 + cb * 16 + r16];
+      xr[cb] = xb + (size_t)(t < 0 ? 0 : t) * K * WB;
+    }
   }
 
-  // One stage: ISSUE = 1 refills the ring with stage st + D - 1 first (steady
-  // state, every earlier stage issued the same instruction count, so the
-  // in-order vmcnt of (D-1) issues is exact); ISSUE = 0 drains the ring.
+  template <int SLOT>
+  __device__ __forceinline__ void issue() {
+    const int kc = ik + irot < ns ? ik + irot : ik + irot - ns;  // K stage loaded now
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      xs[SLOT][cb] = load_raw<WT>(xr[cb] + (size_t)(kc * 4 + wv) * SB);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(src[qq] + (size_t)kc * kRingRowBytes),
+          reinterpret_cast<void*>(ring + SLOT * kG1StageBytes + dst[qq]), 16, 0, kRingAux);
+    stage_fence();
+    if (++ik == ns) {
+      ik = 0;
+      if (++iq < ng) set_task(iq);
+    }
+  }
+
+  // One stage: refill (ISSUE) or drain, then this wave's K-step of the slot.
   template <int SLOT, bool ISSUE>
-  __device__ __forceinline__ void body(int st, int ncb, int r16, int g, f32x4 accg[NCB],
-                                       f32x4 accu[NCB]) {
+  __device__ __forceinline__ void body(f32x4 accg[NCB], f32x4 accu[NCB], int g) {
     if constexpr (ISSUE) {
-      issue<(SLOT + D - 1) % D>(st + D - 1);
+      issue<(SLOT + D - 1) % D>();
       wait_vmcnt<(D - 1) * NI>();
     } else {
       wait_vmcnt<0>();
     }
     wg_barrier();
-    const char* sb = lds + SLOT * kG1StageBytes;
+    const char* sb = ring + SLOT * kG1StageBytes;
     const int b = wv * SB + g * 32;
     Raw<WT> ag, au;
     const int og = ring_off(r16, b), ou = ring_off(16 + r16, b);
@@ -134,202 +180,241 @@ struct G1Ring {
     ag.q[1] = ld16(sb + og + 16);
     au.q[0] = ld16(sb + ou);
     au.q[1] = ld16(sb + ou + 16);
-    auto A = to_op<WT>(ag);
-    auto U = to_op<WT>(au);
+    const auto A = to_op<WT>(ag);
+    const auto U = to_op<WT>(au);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      if (cb < ncb) {
-        auto X = to_op<WT>(xs[SLOT][cb]);
-        accg[cb] = mma(A, X, accg[cb]);
-        accu[cb] = mma(U, X, accu[cb]);
-      }
+      const auto X = to_op<WT>(xs[SLOT][cb]);
+      accg[cb] = mma(A, X, accg[cb]);
+      accu[cb] = mma(U, X, accu[cb]);
     }
-    wg_barrier();
   }
 };
 
-template <int WT, int NCB, int NRB>
-__global__ __launch_bounds__(256, 2) void gemm1_ring_kernel(GemmArgs a) {
+template <int WT, int NCB, int D, int WPC>
+__global__ __launch_bounds__(256, WPC) void gemm1_ring_kernel(GemmArgs a, int GT) {
+  using R_t = PRing<WT, NCB, D>;
+  constexpr int CPG = R_t::CPG, TW = R_t::TW, WB = R_t::WB;
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  constexpr int D = kRingD;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-
-  const int e = nth_active_expert(a.offsets, a.E, blockIdx.y);
-  if (e < 0) return;  // uniform over the workgroup
-  const int seg0 = a.offsets[e], seg1 = a.offsets[e + 1];
-  const int me = segment_count(a.sorted_ids, seg0, seg1, a.P);
-  const int n0 = blockIdx.x * 16 * NRB;
-  const int K = a.K, N = a.N;
-  constexpr int WB = Family<WT>::kBytes;
+  const int K = a.K, N = a.N, bm = a.block_m;
   const int ns = K * WB / kRingRowBytes;
+  const int nrb = N / 16;
+  const int npb = bm > CPG ? bm / CPG : 1;  // column groups per alignment block
+  const long long ntask = (long long)(*a.num_padded / bm) * npb * nrb;
+  const long long G = gridDim.x, w = blockIdx.x;
+  const long long ntw = w < ntask ? (ntask - 1 - w) / G + 1 : 0;  // tasks w, w + G, ...
+  if (ntw <= 0) return;  // uniform over the workgroup
+  // never clamped: the host sizes GT for the longest task list
+  const int ng = ntw < GT ? (int)ntw : GT;
 
-  G1Ring<WT, NCB, NRB> R;
-  R.lds = lds;
-  R.wv = wv;
+  R_t R;
+  R.ring = lds;
+  R.red = reinterpret_cast<float*>(lds + D * kG1StageBytes);
+  int* tab = reinterpret_cast<int*>(lds + D * kG1StageBytes + NCB * kPRedBytesPerCb);
+  R.tab = tab;
+
+  // ---- task table: token row of every column of every task, then each
+  // task's expert, dequant scale, row block, first sorted position and first
+  // K stage.  The first K stage is a hash of the task index: workgroups that
+  // start together would otherwise all read the same 512-byte column of
+  // their rows at the same time (measured on E4M3 weights at 32 and 64
+  // tokens: 8-9% slower when every task starts at stage 0).
+  for (int i = tid; i < ng * CPG; i += 256) {
+    const int q = i / CPG, col = i - q * CPG;
+    const long long t = w + q * G;
+    const int gq = (int)(t / nrb), blk = gq / npb, lc = (gq - blk * npb) * CPG + col;
+    int tok = -1;
+    if (lc < bm) {
+      const int f = a.sorted_ids[(size_t)blk * bm + lc];
+      if (f < a.P) tok = f / a.topk;
+    }
+    tab[q * TW + 5 + col] = tok;
+  }
+  for (int q = tid; q < ng; q += 256) {
+    const long long t = w + q * G;
+    const int gq = (int)(t / nrb), blk = gq / npb;
+    const int e = a.block_expert[blk];
+    float sc = 1.0f;
+    if (WT == DT_E4M3) sc = (*a.sx) * a.w13_scale[e];
+    tab[q * TW] = e;
+    tab[q * TW + 1] = __float_as_int(sc);
+    tab[q * TW + 2] = (int)(t - (long long)gq * nrb);
+    tab[q * TW + 3] = blk * bm + (gq - blk * npb) * CPG;
+    tab[q * TW + 4] = (int)((((unsigned)t * 2654435761u) >> 16) % (unsigned)ns);
+  }
+  __syncthreads();
+
+  R.w13 = reinterpret_cast<const char*>(a.w13);
+  R.xb = reinterpret_cast<const char*>(a.x) + g * 32;
+  R.K = K;
+  R.N = N;
   R.ns = ns;
-  R.rbstride = (size_t)16 * K * WB;
-  const char* w13 = reinterpret_cast<const char*>(a.w13);
-  {
-    const int lrow = lane >> 5;
-    const int lb = ((lane & 31) << 4) ^ (lrow << 7);
+  R.wv = wv;
+  R.r16 = r16;
+  R.lrow = lane >> 5;
+  R.lb = ((lane & 31) << 4) ^ (R.lrow << 7);
+  R.ng = ng;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int blk = 4 * wv + q;
-      const int r = 2 * blk + lrow;
-      const int grow = (r < 16) ? (n0 + r) : (N + n0 + r - 16);
-      R.src[q] = w13 + ((size_t)e * 2 * N + grow) * K * WB + lb;
-      R.dst[q] = blk * kPairStride;
-    }
-  }
-  const char* xb = reinterpret_cast<const char*>(a.x) + g * 32;
+  for (int qq = 0; qq < 4; ++qq) R.dst[qq] = (4 * wv + qq) * kPairStride;
+  R.iq = 0;
+  R.ik = 0;
+  R.set_task(0);
 
-  float scale = 1.0f;
-  if (WT == DT_E4M3) scale = (*a.sx) * a.w13_scale[e];
+  int cq = 0, ck = 0;  // compute cursor: table row, stage within the task
   float hmax = 0.0f;
-  float* red = reinterpret_cast<float*>(lds);  // reused after the ring drains
+  f32x4 accg[NCB], accu[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) accg[cb] = accu[cb] = f32x4{0, 0, 0, 0};
 
-  for (int c0 = 0; c0 < me; c0 += 16 * NCB) {
-    const int ncb = min(NCB, (me - c0 + 15) / 16);
+  // end of a task: waves 1..3 leave their partial sums, wave 0 adds them to
+  // its own and stores the task's 16 x CPG block of h
+  auto finish = [&]() __attribute__((always_inline)) {
+    float* red = R.red;
+    if (wv > 0) {
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const int col = c0 + cb * 16 + r16;
-      const int f = a.sorted_ids[seg0 + (col < me ? col : 0)];
-      R.xr[cb] = xb + (size_t)(f / a.topk) * K * WB;
-    }
-    f32x4 accg[NRB][NCB], accu[NRB][NCB];
+      for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) accg[rb][cb] = accu[rb][cb] = f32x4{0, 0, 0, 0};
-    // stage s of the sequence: slot SL, refill (IS) or drain; row block 1's
-    // stages accumulate into its own registers
-    auto stage = [&](auto slot, auto is, int s) {
-      constexpr int SL = decltype(slot)::value;
-      constexpr bool IS = decltype(is)::value;
-      if (NRB == 1 || s < ns)
-        R.template body<SL, IS>(s, ncb, r16, g, accg[0], accu[0]);
-      else
-        R.template body<SL, IS>(s, ncb, r16, g, accg[NRB - 1], accu[NRB - 1]);
-    };
-    using Refill = std::true_type;
-    using Drain = std::false_type;
-    const int total = NRB * ns;
-
-    // prologue: stages 0 .. D - 2
-    static_for<0, D - 1>([&](auto i) { R.template issue<decltype(i)::value>(decltype(i)::value); });
-    // steady state: whole trips of D stages that all refill (total >= D)
-    const int n_issue = total - (D - 1);  // stages that refill the ring
-    int st = 0;
-    for (; st + D <= n_issue; st += D)
-      static_for<0, D>([&](auto i) { stage(i, Refill{}, st + decltype(i)::value); });
-    // the last n_issue % D refilling stages, then D - 1 draining ones; slot =
-    // stage % D is static in every branch
-    const int rem = n_issue - st;  // 0 .. D - 1
-    static_for<0, D>([&](auto rr) {
-      constexpr int RR = decltype(rr)::value;
-      if (rem == RR) {
-        static_for<0, RR>([&](auto i) { stage(i, Refill{}, st + decltype(i)::value); });
-        static_for<0, D - 1>([&](auto j) {
-          constexpr int J = decltype(j)::value;
-          stage(std::integral_constant<int, (RR + J) % D>{}, Drain{}, st + RR + J);
-        });
-      }
-    });
-
-    // reduce the 4 K-slices of each row block (the ring is drained: every
-    // body ended with a barrier)
-    static_for<0, NRB>([&](auto rbc) {
-    constexpr int RB = decltype(rbc)::value;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        red[((((wv * 2 + 0) * NCB + cb) * 4 + i) << 6) + lane] = accg[RB][cb][i];
-        red[((((wv * 2 + 1) * NCB + cb) * 4 + i) << 6) + lane] = accu[RB][cb][i];
-      }
-    __syncthreads();
-    for (int cb = wv; cb < ncb; cb += 4) {
-      const int col = c0 + cb * 16 + r16;
-      float h[4], g4[4], u4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float gs = 0.0f, us = 0.0f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          gs += red[((((w * 2 + 0) * NCB + cb) * 4 + i) << 6) + lane];
-          us += red[((((w * 2 + 1) * NCB + cb) * 4 + i) << 6) + lane];
+        for (int i = 0; i < 4; ++i) {
+          red[(((((wv - 1) * 2 + 0) * NCB + cb) * 4 + i) << 6) + lane] = accg[cb][i];
+          red[(((((wv - 1) * 2 + 1) * NCB + cb) * 4 + i) << 6) + lane] = accu[cb][i];
         }
-        g4[i] = gs * scale;
-        u4[i] = us * scale;
-        h[i] = silu(g4[i]) * u4[i];
-      }
-      if (a.probe) {
-        if (col < me) probe_store(a, (size_t)(seg0 + col), n0 + 16 * RB + 4 * g, g4, u4);
-      } else if (col < me) {
-        const size_t idx = (size_t)(seg0 + col) * N + n0 + 16 * RB + 4 * g;
-        if (WT == DT_E4M3) {
-          st16(reinterpret_cast<float*>(a.h) + idx,
-               i32x4{__float_as_int(h[0]), __float_as_int(h[1]), __float_as_int(h[2]),
-                     __float_as_int(h[3])});
+    }
+    wg_barrier();  // also the stage's closing barrier
+    if (wv == 0) {
+      const int* row = tab + cq * TW;
+      const float scale = __int_as_float(row[1]);
+      const int n0 = row[2] * 16;
+      const size_t pos0 = (size_t)row[3];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) hmax = fmaxf(hmax, __builtin_fabsf(h[i]));
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int col = cb * 16 + r16;
+        const int t = row[5 + col];
+        float h[4], g4[4], u4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float gs = accg[cb][i], us = accu[cb][i];
+#pragma unroll
+          for (int w2 = 0; w2 < 3; ++w2) {
+            gs += red[((((w2 * 2 + 0) * NCB + cb) * 4 + i) << 6) + lane];
+            us += red[((((w2 * 2 + 1) * NCB + cb) * 4 + i) << 6) + lane];
+          }
+          g4[i] = gs * scale;
+          u4[i] = us * scale;
+          h[i] = silu(g4[i]) * u4[i];
+        }
+        if (t >= 0) {
+          const size_t p = pos0 + col;
+          if (a.probe) {
+            probe_store(a, p, n0 + 4 * g, g4, u4);
+          } else if (WT == DT_E4M3) {
+            st16(reinterpret_cast<float*>(a.h) + p * N + n0 + 4 * g,
+                 i32x4{__float_as_int(h[0]), __float_as_int(h[1]), __float_as_int(h[2]),
+                       __float_as_int(h[3])});
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hmax = fmaxf(hmax, __builtin_fabsf(h[i]));
+          } else {
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.h) + p * N + n0 + 4 * g) =
+                make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) accg[cb] = accu[cb] = f32x4{0, 0, 0, 0};
+    ++cq;
+  };
+
+  // Stage p: slot p % D, refilled with stage p + D - 1 while one remains.
+  // Whole trips of D stages keep every slot index static (the x fragments
+  // live in registers); the tail trip checks p against the total.
+  const int total = ng * ns;  // >= ns >= D
+  static_for<0, D - 1>([&](auto i) { R.template issue<decltype(i)::value>(); });
+  for (int st = 0; st < total; st += D) {
+    static_for<0, D>([&](auto i) __attribute__((always_inline)) {
+      constexpr int SL = decltype(i)::value;
+      const int p = st + SL;
+      if (p < total) {
+        if (p + D - 1 < total)
+          R.template body<SL, true>(accg, accu, g);
+        else
+          R.template body<SL, false>(accg, accu, g);
+        if (++ck == ns) {
+          ck = 0;
+          finish();
         } else {
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.h) + idx) =
-              make_uint2(pack_bf16x2(h[0], h[1]),
-                         pack_bf16x2(h[2], h[3]));
+          wg_barrier();
         }
       }
-    }
-    __syncthreads();  // red aliases the ring: drain before it is reused
     });
   }
-  if (WT == DT_E4M3) {
+
+  if (WT == DT_E4M3 && wv == 0) {
     hmax = wave_max(hmax);
     if (lane == 0 && hmax > 0.0f) atomicMax(a.hmax_bits, __float_as_uint(hmax));
   }
+}
+
+// Launch: WPC workgroups per CU, the task table sized for the longest task
+// list a workgroup can get (capacity bound / G, rounded up, plus one).
+template <int WT, int NCB, int D, int WPC>
+struct G1Ring {
+  using R_t = PRing<WT, NCB, D>;
+  static int table_rows(const GemmArgs& a) {
+    const int bm = a.block_m;
+    const long long npb = bm > R_t::CPG ? bm / R_t::CPG : 1;
+    const long long cap = (long long)a.P + (long long)min(a.E, a.P) * (bm - 1);
+    const long long ntask = (cap + bm - 1) / bm * npb * (a.N / 16);
+    const long long G = (long long)WPC * device_cu_count();
+    return (int)((ntask + G - 1) / G) + 1;
+  }
+  static size_t lds(const GemmArgs& a) {
+    return (size_t)D * kG1StageBytes + NCB * kPRedBytesPerCb +
+           (size_t)table_rows(a) * R_t::TW * sizeof(int);
+  }
+  static bool fits(const GemmArgs& a) { return lds(a) <= (size_t)160 * 1024 / WPC; }
+  static int launch(const GemmArgs& a, hipStream_t st) {
+    const size_t bytes = lds(a);
+    static size_t attr = 0;  // largest dynamic LDS size enabled so far
+    if (bytes > attr) {
+      int err = (int)hipFuncSetAttribute((const void*)gemm1_ring_kernel<WT, NCB, D, WPC>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+      if (err) return err;
+      attr = bytes;
+    }
+    hipLaunchKernelGGL((gemm1_ring_kernel<WT, NCB, D, WPC>), dim3(WPC * device_cu_count()),
+                       dim3(256), bytes, st, a, table_rows(a));
+    return (int)hipGetLastError();
+  }
+};
+
+// One column block per task for 16-row alignment blocks, two for wider
+// ones; two workgroups per CU (measured: one workgroup with an 8-stage ring
+// streams 25-40% slower), one when the task table does not leave room for two.
+template <int WT, int NCB>
+static int g1r_try(const GemmArgs& a, hipStream_t st, bool run) {
+  if (G1Ring<WT, NCB, kRingD, 2>::fits(a)) return run ? G1Ring<WT, NCB, kRingD, 2>::launch(a, st) : 0;
+  if (G1Ring<WT, NCB, kRingD, 1>::fits(a)) return run ? G1Ring<WT, NCB, kRingD, 1>::launch(a, st) : 0;
+  return -1;
+}
+
+template <int WT>
+static int g1r_dispatch(const GemmArgs& a, hipStream_t st, bool run) {
+  return a.block_m <= 16 ? g1r_try<WT, 1>(a, st, run) : g1r_try<WT, 2>(a, st, run);
 }
 
 bool gemm1_ring_applies(const GemmArgs& a) {
   if (!((a.wt == DT_BF16 && a.xt == DT_BF16) || (a.wt == DT_E4M3 && a.xt == DT_E4M3)))
     return false;
   const long long row = (long long)a.K * (a.wt == DT_BF16 ? 2 : 1);
-  return row % kRingRowBytes == 0 && row / kRingRowBytes >= kRingD;
-}
-
-template <int WT, int NCB, int NRB>
-static int g1r_launch(const GemmArgs& a, hipStream_t st) {
-  const size_t ring = (size_t)kRingD * kG1StageBytes;
-  const size_t red = (size_t)4 * 2 * NCB * 4 * kWave * sizeof(float);
-  const size_t lds = ring > red ? ring : red;
-  static bool attr = false;
-  if (!attr) {
-    int err = (int)hipFuncSetAttribute((const void*)gemm1_ring_kernel<WT, NCB, NRB>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err) return err;
-    attr = true;
-  }
-  dim3 grid(a.N / (16 * NRB), min(a.E, a.P));
-  hipLaunchKernelGGL((gemm1_ring_kernel<WT, NCB, NRB>), grid, dim3(256), lds, st, a);
-  return (int)hipGetLastError();
-}
-
-// Two row blocks per workgroup for E4M3 with one token column block (half
-// the bytes per row, so one row block is too short a stream; measured 5-7%
-// faster at T = 1-16).  With two column blocks the second row block's
-// accumulators no longer fit two workgroups per CU without spilling, which
-// costs more than it gains, so bf16 and wider batches keep one.
-template <int WT>
-static int g1r_dispatch(const GemmArgs& a, hipStream_t st, int ncb) {
-  if constexpr (WT == DT_E4M3) {
-    if (ncb <= 1 && a.N % 32 == 0) return g1r_launch<WT, 1, 2>(a, st);
-  }
-  return ncb <= 1 ? g1r_launch<WT, 1, 1>(a, st) : g1r_launch<WT, 2, 1>(a, st);
+  if (row % kRingRowBytes != 0 || row / kRingRowBytes < kRingD || a.N % 16 != 0) return false;
+  return (a.wt == DT_E4M3 ? g1r_dispatch<DT_E4M3>(a, nullptr, false)
+                          : g1r_dispatch<DT_BF16>(a, nullptr, false)) == 0;
 }
 
 int launch_gemm1_ring(const GemmArgs& a, hipStream_t st) {
-  const int ncb = min((min(a.M, kStreamMaxM) + 15) / 16, kRingNcbMax);
-  return a.wt == DT_E4M3 ? g1r_dispatch<DT_E4M3>(a, st, ncb) : g1r_dispatch<DT_BF16>(a, st, ncb);
+  return a.wt == DT_E4M3 ? g1r_dispatch<DT_E4M3>(a, st, true) : g1r_dispatch<DT_BF16>(a, st, true);
 }
 
 }  // namespace moe

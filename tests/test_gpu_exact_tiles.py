@@ -52,6 +52,9 @@ GATE_UP = [
     (0, torch.bfloat16, 5, 2048, 256, 8, 2, 16),     # ring, one column block
     (0, torch.bfloat16, 40, 2048, 256, 8, 2, 16),    # ring, two column blocks
     (0, torch.float8_e4m3fn, 40, 2048, 256, 8, 2, 16),
+    (0, torch.bfloat16, 40, 2048, 256, 8, 2, 32),    # ring, 32-column token groups
+    (0, torch.float8_e4m3fn, 64, 2048, 256, 8, 2, 64),  # two groups per 64-row block
+    (0, torch.bfloat16, 1, 2048, 256, 8, 2, 16),     # fewer tasks than workgroups
     (0, torch.float32, 12, 512, 256, 8, 2, 16),      # stream kernel (f32 weights)
     (1, torch.bfloat16, 200, 1024, 256, 8, 2, 128),  # prefill kernel, 256 x 128 tiles
     (1, torch.float8_e4m3fn, 200, 1024, 256, 8, 2, 256),  # 256 x 256 tiles

@@ -245,6 +245,26 @@ def test_forward_small_matches_oracle(name, wl, T, Hd, Id, Ed, kd, bm):
     assert err <= tol, err
 
 
+# Decode shapes whose gate/up task table does not fit beside two rings per
+# CU (64 tokens, 1024 experts, 32-row alignment blocks: the capacity bound is
+# 512 blocks x 64 row blocks = 32768 tasks, 65 per workgroup at 512
+# workgroups, 9.4 KiB of table next to 65 KiB of ring and 12 KiB of partial
+# sums), so the layer runs the one-workgroup-per-CU launch of the same kernel.
+@pytest.mark.parametrize("wl", ["decode_bf16", "decode_fp8"])
+def test_forward_gate_up_ring_one_workgroup_per_cu(wl):
+    w = W[wl]
+    d = inputs.make_inputs(w, 64, device=DEV, H=1024, I=1024, E=1024, topk=8)
+    a2 = 0.05 if w.fp8_act else None  # static h scale: the oracle needs only 4 tokens' experts
+    layer, out = H.run_gpu(d, block_m=32, a2_scale=a2)
+    tokens = np.array([0, 21, 42, 63])
+    ref, rids, _, _ = H.oracle_forward(d, tokens=tokens, a2_scale=a2)
+    assert np.array_equal(layer.topk_ids.cpu().numpy(), rids)
+    err = H.row_rel_err(H.to_f64(out)[tokens], ref)
+    tol = H.FP8_TOL if w.fp8_act else H.BF16_TOL
+    H.say(f"  {wl} E=1024 bm=32: sampled rows max rel err {err:.3e}")
+    assert err <= tol, err
+
+
 def test_forward_fp8_static_scales():
     d = inputs.make_inputs(W["decode_fp8"], 24, device=DEV, H=512, I=256, E=16, topk=4)
     layer, out = H.run_gpu(d, a1_scale=0.02, a2_scale=0.01)
