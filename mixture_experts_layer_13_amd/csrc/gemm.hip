@@ -633,26 +633,46 @@ __global__ __launch_bounds__(256) void combine_kernel(GemmArgs a) {
   const int t = blockIdx.x;
   const int n = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (n >= K) return;
+  constexpr int Q = (OT == DT_BF16) ? 1 : 2;  // 16-byte loads per row slice
   float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int j = 0; j < a.topk; ++j) {
-    const int pos = a.pair_pos[(size_t)t * a.topk + j];
-    if (pos < 0) continue;
-    const float w = a.topk_w[(size_t)t * a.topk + j];
-    const size_t at = (size_t)pos * K + n;
-    if (OT == DT_BF16) {
-      const i32x4 q = ld16(reinterpret_cast<const uint16_t*>(a.y) + at);
+  // eight slots at a time: their rows are all requested before the first is
+  // added, then added in slot order
+  for (int j0 = 0; j0 < a.topk; j0 += 8) {
+    int pos[8];
+    float w[8];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        v[2 * c] += w * bf16_bits_to_f32((uint32_t)q[c] & 0xffffu);
-        v[2 * c + 1] += w * bf16_bits_to_f32((uint32_t)q[c] >> 16);
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = j0 + j < a.topk;
+      pos[j] = ok ? a.pair_pos[(size_t)t * a.topk + j0 + j] : -1;
+      w[j] = ok ? a.topk_w[(size_t)t * a.topk + j0 + j] : 0.0f;
+    }
+    i32x4 q[8][Q];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const size_t at = (size_t)(pos[j] < 0 ? 0 : pos[j]) * K + n;
+#pragma unroll
+      for (int c = 0; c < Q; ++c) {
+        q[j][c] = i32x4{0, 0, 0, 0};
+        if (pos[j] >= 0)
+          q[j][c] = (OT == DT_BF16) ? ld16(reinterpret_cast<const uint16_t*>(a.y) + at)
+                                    : ld16(reinterpret_cast<const float*>(a.y) + at + 4 * c);
       }
-    } else {
-      const i32x4 q0 = ld16(reinterpret_cast<const float*>(a.y) + at);
-      const i32x4 q1 = ld16(reinterpret_cast<const float*>(a.y) + at + 4);
+    }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        v[c] += w * __int_as_float(q0[c]);
-        v[4 + c] += w * __int_as_float(q1[c]);
+    for (int j = 0; j < 8; ++j) {
+      if (pos[j] < 0) continue;
+      if (OT == DT_BF16) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          v[2 * c] += w[j] * bf16_bits_to_f32((uint32_t)q[j][0][c] & 0xffffu);
+          v[2 * c + 1] += w[j] * bf16_bits_to_f32((uint32_t)q[j][0][c] >> 16);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          v[c] += w[j] * __int_as_float(q[j][0][c]);
+          v[4 + c] += w[j] * __int_as_float(q[j][Q - 1][c]);
+        }
       }
     }
   }
@@ -718,7 +738,6 @@ static int g2s_dispatch(const GemmArgs& a, hipStream_t st) {
 }
 
 int launch_gemm2_stream(const GemmArgs& a, hipStream_t st) {
-  if (gemm2_ring_applies(a)) return launch_gemm2_ring(a, st);
   if (a.wt == DT_E4M3)
     return a.ot == DT_BF16 ? g2s_dispatch<DT_E4M3, DT_BF16>(a, st) : g2s_dispatch<DT_E4M3, DT_F32>(a, st);
   if (a.wt == DT_BF16)

@@ -78,8 +78,8 @@ Layout layout_of(const moe_problem& p) {
   o = up256(o + (size_t)cap * p.N * (fp8 ? 4 : 2));
   L.hq = o;
   if (fp8) o = up256(o + (size_t)cap * p.N);
-  L.y = o;
-  if (!stream_path) o = up256(o + (size_t)cap * p.K * 4);
+  L.y = o;  // per-pair down-projection rows (every path but the f32-weight decode kernel)
+  o = up256(o + (size_t)cap * p.K * 4);
   L.total = o;
   return L;
 }
@@ -330,11 +330,11 @@ moe_status moe_fused_forward(const moe_problem* p, const void* a, const void* w1
   }
 
   if (prof[2]) (void)hipEventRecord((hipEvent_t)prof[2], st);
-  if (stream_path) {
-    err = moe::launch_gemm2_stream(g, st);
+  if (stream_path && !moe::gemm2_ring_applies(g)) {
+    err = moe::launch_gemm2_stream(g, st);  // f32 weights: combine fused
     if (err) return hip_status(err, "down GEMM launch");
   } else {
-    err = moe::launch_gemm2_tile(g, st);
+    err = stream_path ? moe::launch_gemm2_ring(g, st) : moe::launch_gemm2_tile(g, st);
     if (err) return hip_status(err, "down GEMM launch");
     if (prof[3]) (void)hipEventRecord((hipEvent_t)prof[3], st);
     prof[3] = nullptr;

@@ -35,7 +35,6 @@ constexpr int kPairStride = 2 * kRingRowBytes + 16;  // LDS bytes of a 2-row DMA
 constexpr int kG1RingRows = 32;         // 16 gate + 16 up rows
 constexpr int kG1StageBytes = (kG1RingRows / 2) * kPairStride;
 constexpr int kRingAux = 2;             // cache-policy bits of the weight DMA (2: nt)
-constexpr int kRingNcbMax = 2;
 
 __device__ __forceinline__ int ring_off(int r, int b) {
   return (r >> 1) * kPairStride + (r & 1) * kRingRowBytes + (b ^ ((r & 1) << 7));
@@ -80,44 +79,56 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// ------------------------------------------------------------ gate/up ring
+// ------------------------------------------------------------ expert rings
 //
-// One launch of a fixed number of workgroups (WPC per CU) that walk a static
-// list of tasks without draining the ring between them.  Task = (column group, 16-row block): a column group
+// Both expert GEMMs of the decode path: one launch of a fixed number of
+// workgroups (WPC per CU) that walk a static list of tasks without draining
+// the ring between them.  Task = (column group, 32-row block): a column group
 // is 16*NCB consecutive positions of one alignment block (block_m = 16*NCB, or
-// a multiple of it, then one block is several groups), and a row block is
-// gate rows n0..n0+15 with the matching up rows, of the block's expert.  Tasks
-// are numbered group-major; workgroup w takes tasks w, w + G, w + 2G, ... (G
-// workgroups), so every workgroup streams the same number of weight bytes (to
-// one task), the ring fills and drains once per workgroup instead of once per
-// row block, and at any moment the workgroups read neighbouring tasks (the
-// order a one-task-per-workgroup launch would dispatch them in).  Everything a
-// task needs before its first load -- expert, dequant scale, row block, the
-// token row of each column -- is read into an LDS table row when the
-// workgroup starts, so that switching tasks inside the stream reads only LDS
-// and never waits on the vector-memory counter the ring runs on.
+// a multiple of it, then one block is several groups), and the row block is
+// 32 weight rows of the block's expert -- for gate/up (G1) gate rows
+// n0..n0+15 with the matching up rows, for the down projection 32
+// consecutive rows of w2.  Tasks are numbered group-major; workgroup w takes
+// tasks w, w + G, w + 2G, ... (G workgroups), so every workgroup streams the
+// same number of weight bytes (to one task), the ring fills and drains once
+// per workgroup instead of once per row block, and at any moment the
+// workgroups read neighbouring tasks (the order a one-task-per-workgroup
+// launch would dispatch them in).  Everything a task needs before its first
+// load -- expert, dequant scale, row block, the operand row of each column --
+// is read into an LDS table row when the workgroup starts, so that switching
+// tasks inside the stream reads only LDS and never waits on the
+// vector-memory counter the ring runs on.
 //
 // At the end of a task the four K-slices are summed by wave 0 (waves 1..3
 // leave their partial sums in a small LDS area beside the ring) while the
-// other waves already work on the next task's stages.
+// other waves already work on the next task's stages.  Gate/up writes
+// SiLU(gate) * up to h; the down projection writes each pair's 32 output
+// features, dequantised but not yet weighted, to y, and the combine kernel
+// sums the top-k rows of every token with their routing weights.
 
-constexpr int kPRedBytesPerCb = 3 * 2 * 4 * kWave * 4;  // waves 1..3 x gate/up x 4 regs x lanes
+constexpr int kPRedBytesPerCb = 3 * 2 * 4 * kWave * 4;  // waves 1..3 x 2 halves x 4 regs x lanes
 
-template <int WT, int NCB, int D>
+template <int WT, int NCB, int D, bool G1>
 struct PRing {
   static constexpr int SB = 128;          // bytes per K-step of a row
   static constexpr int NI = 4 + 2 * NCB;  // vector-memory instructions per issue
   static constexpr int WB = Family<WT>::kBytes;
   static constexpr int CPG = 16 * NCB;    // columns per group
   // table row: expert, scale bits, row block, first sorted position, K stage
-  // the task starts at, then the token row of every column (-1: padding)
-  static constexpr int TW = CPG + 5;
+  // the task starts at, then one byte per column: 255 for padding, else for
+  // gate/up the token row of x (the decode path has at most 64 tokens); the
+  // down projection reads h at the column's sorted position
+  static constexpr int TW = 5 + CPG / 4;
+  static constexpr int kPad = 255;
   char* ring;
   float* red;
   const int* tab;
-  const char* w13;
-  const char* xb;  // x + this lane's 32-byte offset within a K-step
-  int K, N, ns, wv, r16, lrow, lb, ng;
+  const char* w;   // expert weights [E][rows][kdim]
+  const char* xb;  // operand rows + this lane's 32-byte offset within a K-step
+  size_t wrow;     // bytes of one weight row = bytes of one operand row
+  int wrows;       // weight rows per expert
+  int half;        // G1: row offset of the up half (N)
+  int ns, wv, r16, lrow, lb, ng;
   // issue cursor: table row (task of this workgroup), stage within the task
   int iq, ik;
   int irot;  // K stage the task starts at (tasks walk K from different offsets)
@@ -129,18 +140,28 @@ struct PRing {
   __device__ __forceinline__ void set_task(int q) {
     const int* row = tab + q * TW;
     const int e = row[0], rb = row[2];
-    const int n0 = rb * 16;
     irot = row[4];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const int r = 2 * (4 * wv + qq) + lrow;
-      const int grow = (r < 16) ? (n0 + r) : (N + n0 + r - 16);
-      src[qq] = w13 + ((size_t)e * 2 * N + grow) * K * WB + lb;
+      int grow;
+      if constexpr (G1)
+        grow = (r < 16) ? (16 * rb + r) : (half + 16 * rb + r - 16);
+      else
+        grow = 32 * rb + r;
+      src[qq] = w + ((size_t)e * wrows + grow) * wrow + lb;
     }
+    const uint8_t* col8 = reinterpret_cast<const uint8_t*>(row + 5);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      const int t = row[5 + cb * 16 + r16];
-      xr[cb] = xb + (size_t)(t < 0 ? 0 : t) * K * WB;
+      const int c = cb * 16 + r16;
+      int xrow;
+      if constexpr (G1) {
+        xrow = col8[c] == kPad ? 0 : col8[c];
+      } else {
+        xrow = row[3] + c;  // padding rows of h exist (never written): their columns are dropped
+      }
+      xr[cb] = xb + (size_t)xrow * wrow;
     }
   }
 
@@ -164,7 +185,7 @@ struct PRing {
 
   // One stage: refill (ISSUE) or drain, then this wave's K-step of the slot.
   template <int SLOT, bool ISSUE>
-  __device__ __forceinline__ void body(f32x4 accg[NCB], f32x4 accu[NCB], int g) {
+  __device__ __forceinline__ void body(f32x4 acc0[NCB], f32x4 acc1[NCB], int g) {
     if constexpr (ISSUE) {
       issue<(SLOT + D - 1) % D>();
       wait_vmcnt<(D - 1) * NI>();
@@ -174,33 +195,36 @@ struct PRing {
     wg_barrier();
     const char* sb = ring + SLOT * kG1StageBytes;
     const int b = wv * SB + g * 32;
-    Raw<WT> ag, au;
-    const int og = ring_off(r16, b), ou = ring_off(16 + r16, b);
-    ag.q[0] = ld16(sb + og);
-    ag.q[1] = ld16(sb + og + 16);
-    au.q[0] = ld16(sb + ou);
-    au.q[1] = ld16(sb + ou + 16);
-    const auto A = to_op<WT>(ag);
-    const auto U = to_op<WT>(au);
+    Raw<WT> a0, a1;
+    const int o0 = ring_off(r16, b), o1 = ring_off(16 + r16, b);
+    a0.q[0] = ld16(sb + o0);
+    a0.q[1] = ld16(sb + o0 + 16);
+    a1.q[0] = ld16(sb + o1);
+    a1.q[1] = ld16(sb + o1 + 16);
+    const auto A0 = to_op<WT>(a0);
+    const auto A1 = to_op<WT>(a1);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       const auto X = to_op<WT>(xs[SLOT][cb]);
-      accg[cb] = mma(A, X, accg[cb]);
-      accu[cb] = mma(U, X, accu[cb]);
+      acc0[cb] = mma(A0, X, acc0[cb]);
+      acc1[cb] = mma(A1, X, acc1[cb]);
     }
   }
 };
 
-template <int WT, int NCB, int D, int WPC>
-__global__ __launch_bounds__(256, WPC) void gemm1_ring_kernel(GemmArgs a, int GT) {
-  using R_t = PRing<WT, NCB, D>;
+template <int WT, int NCB, int D, int WPC, bool G1>
+__global__ __launch_bounds__(256, WPC) void ring_gemm_kernel(GemmArgs a, int GT) {
+  using R_t = PRing<WT, NCB, D, G1>;
   constexpr int CPG = R_t::CPG, TW = R_t::TW, WB = R_t::WB;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const int K = a.K, N = a.N, bm = a.block_m;
-  const int ns = K * WB / kRingRowBytes;
-  const int nrb = N / 16;
+  const int bm = a.block_m;
+  // gate/up: [E][2N][K] weights, out rows N per half, K-dim K; down: [E][K][N]
+  // weights, 32 of its K rows per task, K-dim N
+  const int kdim = G1 ? a.K : a.N;
+  const int ns = kdim * WB / kRingRowBytes;
+  const int nrb = G1 ? a.N / 16 : a.K / 32;
   const int npb = bm > CPG ? bm / CPG : 1;  // column groups per alignment block
   const long long ntask = (long long)(*a.num_padded / bm) * npb * nrb;
   const long long G = gridDim.x, w = blockIdx.x;
@@ -215,29 +239,29 @@ __global__ __launch_bounds__(256, WPC) void gemm1_ring_kernel(GemmArgs a, int GT
   int* tab = reinterpret_cast<int*>(lds + D * kG1StageBytes + NCB * kPRedBytesPerCb);
   R.tab = tab;
 
-  // ---- task table: token row of every column of every task, then each
-  // task's expert, dequant scale, row block, first sorted position and first
-  // K stage.  The first K stage is a hash of the task index: workgroups that
-  // start together would otherwise all read the same 512-byte column of
-  // their rows at the same time (measured on E4M3 weights at 32 and 64
-  // tokens: 8-9% slower when every task starts at stage 0).
+  // ---- task table: each task's expert, dequant scale, row block, first
+  // sorted position and first K stage, then its column bytes.  The
+  // first K stage is a hash of the task index: workgroups that start
+  // together would otherwise all read the same 512-byte column of their rows
+  // at the same time (measured on E4M3 gate/up weights at 32 and 64 tokens:
+  // 8-9% slower when every task starts at stage 0).
   for (int i = tid; i < ng * CPG; i += 256) {
     const int q = i / CPG, col = i - q * CPG;
     const long long t = w + q * G;
     const int gq = (int)(t / nrb), blk = gq / npb, lc = (gq - blk * npb) * CPG + col;
-    int tok = -1;
+    int b = R_t::kPad;
     if (lc < bm) {
-      const int f = a.sorted_ids[(size_t)blk * bm + lc];
-      if (f < a.P) tok = f / a.topk;
+      const int f = a.sorted_ids[blk * bm + lc];
+      if (f < a.P) b = G1 ? f / a.topk : 0;
     }
-    tab[q * TW + 5 + col] = tok;
+    reinterpret_cast<uint8_t*>(tab + q * TW + 5)[col] = (uint8_t)b;
   }
   for (int q = tid; q < ng; q += 256) {
     const long long t = w + q * G;
     const int gq = (int)(t / nrb), blk = gq / npb;
     const int e = a.block_expert[blk];
     float sc = 1.0f;
-    if (WT == DT_E4M3) sc = (*a.sx) * a.w13_scale[e];
+    if (WT == DT_E4M3) sc = G1 ? (*a.sx) * a.w13_scale[e] : (*a.sh) * a.w2_scale[e];
     tab[q * TW] = e;
     tab[q * TW + 1] = __float_as_int(sc);
     tab[q * TW + 2] = (int)(t - (long long)gq * nrb);
@@ -246,10 +270,11 @@ __global__ __launch_bounds__(256, WPC) void gemm1_ring_kernel(GemmArgs a, int GT
   }
   __syncthreads();
 
-  R.w13 = reinterpret_cast<const char*>(a.w13);
-  R.xb = reinterpret_cast<const char*>(a.x) + g * 32;
-  R.K = K;
-  R.N = N;
+  R.w = reinterpret_cast<const char*>(G1 ? a.w13 : a.w2);
+  R.xb = reinterpret_cast<const char*>(G1 ? a.x : a.hq) + g * 32;
+  R.wrow = (size_t)kdim * WB;
+  R.wrows = G1 ? 2 * a.N : a.K;
+  R.half = a.N;
   R.ns = ns;
   R.wv = wv;
   R.r16 = r16;
@@ -264,12 +289,12 @@ __global__ __launch_bounds__(256, WPC) void gemm1_ring_kernel(GemmArgs a, int GT
 
   int cq = 0, ck = 0;  // compute cursor: table row, stage within the task
   float hmax = 0.0f;
-  f32x4 accg[NCB], accu[NCB];
+  f32x4 acc0[NCB], acc1[NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) accg[cb] = accu[cb] = f32x4{0, 0, 0, 0};
+  for (int cb = 0; cb < NCB; ++cb) acc0[cb] = acc1[cb] = f32x4{0, 0, 0, 0};
 
   // end of a task: waves 1..3 leave their partial sums, wave 0 adds them to
-  // its own and stores the task's 16 x CPG block of h
+  // its own and stores the task's 32 x CPG block
   auto finish = [&]() __attribute__((always_inline)) {
     float* red = R.red;
     if (wv > 0) {
@@ -277,37 +302,42 @@ __global__ __launch_bounds__(256, WPC) void gemm1_ring_kernel(GemmArgs a, int GT
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          red[(((((wv - 1) * 2 + 0) * NCB + cb) * 4 + i) << 6) + lane] = accg[cb][i];
-          red[(((((wv - 1) * 2 + 1) * NCB + cb) * 4 + i) << 6) + lane] = accu[cb][i];
+          red[(((((wv - 1) * 2 + 0) * NCB + cb) * 4 + i) << 6) + lane] = acc0[cb][i];
+          red[(((((wv - 1) * 2 + 1) * NCB + cb) * 4 + i) << 6) + lane] = acc1[cb][i];
         }
     }
     wg_barrier();  // also the stage's closing barrier
     if (wv == 0) {
       const int* row = tab + cq * TW;
       const float scale = __int_as_float(row[1]);
-      const int n0 = row[2] * 16;
+      const int rb = row[2];
       const size_t pos0 = (size_t)row[3];
+      const uint8_t* col8 = reinterpret_cast<const uint8_t*>(row + 5);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         const int col = cb * 16 + r16;
-        const int t = row[5 + col];
-        float h[4], g4[4], u4[4];
+        const bool real = col8[col] != R_t::kPad;
+        float v0[4], v1[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float gs = accg[cb][i], us = accu[cb][i];
+          float s0 = acc0[cb][i], s1 = acc1[cb][i];
 #pragma unroll
           for (int w2 = 0; w2 < 3; ++w2) {
-            gs += red[((((w2 * 2 + 0) * NCB + cb) * 4 + i) << 6) + lane];
-            us += red[((((w2 * 2 + 1) * NCB + cb) * 4 + i) << 6) + lane];
+            s0 += red[((((w2 * 2 + 0) * NCB + cb) * 4 + i) << 6) + lane];
+            s1 += red[((((w2 * 2 + 1) * NCB + cb) * 4 + i) << 6) + lane];
           }
-          g4[i] = gs * scale;
-          u4[i] = us * scale;
-          h[i] = silu(g4[i]) * u4[i];
+          v0[i] = s0 * scale;
+          v1[i] = s1 * scale;
         }
-        if (t >= 0) {
-          const size_t p = pos0 + col;
+        if (!real) continue;
+        const size_t p = pos0 + col;
+        if constexpr (G1) {
+          const int N = a.N, n0 = 16 * rb;
+          float h[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) h[i] = silu(v0[i]) * v1[i];
           if (a.probe) {
-            probe_store(a, p, n0 + 4 * g, g4, u4);
+            probe_store(a, p, n0 + 4 * g, v0, v1);
           } else if (WT == DT_E4M3) {
             st16(reinterpret_cast<float*>(a.h) + p * N + n0 + 4 * g,
                  i32x4{__float_as_int(h[0]), __float_as_int(h[1]), __float_as_int(h[2]),
@@ -318,28 +348,43 @@ __global__ __launch_bounds__(256, WPC) void gemm1_ring_kernel(GemmArgs a, int GT
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.h) + p * N + n0 + 4 * g) =
                 make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
           }
+        } else {
+          const size_t o = p * a.K + 32 * rb + 4 * g;  // rows 4g.. and 16 + 4g.. of the block
+          if (a.ot == DT_BF16) {
+            uint16_t* y = reinterpret_cast<uint16_t*>(a.y);
+            *reinterpret_cast<uint2*>(y + o) = make_uint2(pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]));
+            *reinterpret_cast<uint2*>(y + o + 16) = make_uint2(pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]));
+          } else {
+            float* y = reinterpret_cast<float*>(a.y);
+            st16(y + o, i32x4{__float_as_int(v0[0]), __float_as_int(v0[1]), __float_as_int(v0[2]),
+                              __float_as_int(v0[3])});
+            st16(y + o + 16, i32x4{__float_as_int(v1[0]), __float_as_int(v1[1]), __float_as_int(v1[2]),
+                                   __float_as_int(v1[3])});
+          }
         }
       }
     }
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) accg[cb] = accu[cb] = f32x4{0, 0, 0, 0};
+    for (int cb = 0; cb < NCB; ++cb) acc0[cb] = acc1[cb] = f32x4{0, 0, 0, 0};
     ++cq;
   };
 
   // Stage p: slot p % D, refilled with stage p + D - 1 while one remains.
-  // Whole trips of D stages keep every slot index static (the x fragments
-  // live in registers); the tail trip checks p against the total.
-  const int total = ng * ns;  // >= ns >= D
-  static_for<0, D - 1>([&](auto i) { R.template issue<decltype(i)::value>(); });
+  // Whole trips of D stages keep every slot index static (the operand
+  // fragments live in registers); the tail trip checks p against the total.
+  const int total = ng * ns;
+  static_for<0, D - 1>([&](auto i) {
+    if (decltype(i)::value < total) R.template issue<decltype(i)::value>();
+  });
   for (int st = 0; st < total; st += D) {
     static_for<0, D>([&](auto i) __attribute__((always_inline)) {
       constexpr int SL = decltype(i)::value;
       const int p = st + SL;
       if (p < total) {
         if (p + D - 1 < total)
-          R.template body<SL, true>(accg, accu, g);
+          R.template body<SL, true>(acc0, acc1, g);
         else
-          R.template body<SL, false>(accg, accu, g);
+          R.template body<SL, false>(acc0, acc1, g);
         if (++ck == ns) {
           ck = 0;
           finish();
@@ -350,7 +395,7 @@ __global__ __launch_bounds__(256, WPC) void gemm1_ring_kernel(GemmArgs a, int GT
     });
   }
 
-  if (WT == DT_E4M3 && wv == 0) {
+  if (G1 && WT == DT_E4M3 && wv == 0) {
     hmax = wave_max(hmax);
     if (lane == 0 && hmax > 0.0f) atomicMax(a.hmax_bits, __float_as_uint(hmax));
   }
@@ -358,14 +403,14 @@ __global__ __launch_bounds__(256, WPC) void gemm1_ring_kernel(GemmArgs a, int GT
 
 // Launch: WPC workgroups per CU, the task table sized for the longest task
 // list a workgroup can get (capacity bound / G, rounded up, plus one).
-template <int WT, int NCB, int D, int WPC>
-struct G1Ring {
-  using R_t = PRing<WT, NCB, D>;
+template <int WT, int NCB, int D, int WPC, bool G1>
+struct RingGemm {
+  using R_t = PRing<WT, NCB, D, G1>;
   static int table_rows(const GemmArgs& a) {
     const int bm = a.block_m;
     const long long npb = bm > R_t::CPG ? bm / R_t::CPG : 1;
     const long long cap = (long long)a.P + (long long)min(a.E, a.P) * (bm - 1);
-    const long long ntask = (cap + bm - 1) / bm * npb * (a.N / 16);
+    const long long ntask = (cap + bm - 1) / bm * npb * (G1 ? a.N / 16 : a.K / 32);
     const long long G = (long long)WPC * device_cu_count();
     return (int)((ntask + G - 1) / G) + 1;
   }
@@ -378,12 +423,12 @@ struct G1Ring {
     const size_t bytes = lds(a);
     static size_t attr = 0;  // largest dynamic LDS size enabled so far
     if (bytes > attr) {
-      int err = (int)hipFuncSetAttribute((const void*)gemm1_ring_kernel<WT, NCB, D, WPC>,
+      int err = (int)hipFuncSetAttribute((const void*)ring_gemm_kernel<WT, NCB, D, WPC, G1>,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
       if (err) return err;
       attr = bytes;
     }
-    hipLaunchKernelGGL((gemm1_ring_kernel<WT, NCB, D, WPC>), dim3(WPC * device_cu_count()),
+    hipLaunchKernelGGL((ring_gemm_kernel<WT, NCB, D, WPC, G1>), dim3(WPC * device_cu_count()),
                        dim3(256), bytes, st, a, table_rows(a));
     return (int)hipGetLastError();
   }
@@ -391,374 +436,52 @@ struct G1Ring {
 
 // One column block per task for 16-row alignment blocks, two for wider
 // ones; two workgroups per CU (measured: one workgroup with an 8-stage ring
-// streams 25-40% slower), one when the task table does not leave room for two.
-template <int WT, int NCB>
-static int g1r_try(const GemmArgs& a, hipStream_t st, bool run) {
-  if (G1Ring<WT, NCB, kRingD, 2>::fits(a)) return run ? G1Ring<WT, NCB, kRingD, 2>::launch(a, st) : 0;
-  if (G1Ring<WT, NCB, kRingD, 1>::fits(a)) return run ? G1Ring<WT, NCB, kRingD, 1>::launch(a, st) : 0;
+// streams 25-40% slower), one when the task table does not leave room for
+// two.  run = false only asks whether a launch would fit (0) or not (-1).
+template <int WT, int NCB, bool G1>
+static int ring_try(const GemmArgs& a, hipStream_t st, bool run) {
+  if (RingGemm<WT, NCB, kRingD, 2, G1>::fits(a))
+    return run ? RingGemm<WT, NCB, kRingD, 2, G1>::launch(a, st) : 0;
+  if (RingGemm<WT, NCB, kRingD, 1, G1>::fits(a))
+    return run ? RingGemm<WT, NCB, kRingD, 1, G1>::launch(a, st) : 0;
   return -1;
 }
 
-template <int WT>
-static int g1r_dispatch(const GemmArgs& a, hipStream_t st, bool run) {
-  return a.block_m <= 16 ? g1r_try<WT, 1>(a, st, run) : g1r_try<WT, 2>(a, st, run);
+template <bool G1>
+static int ring_dispatch(const GemmArgs& a, hipStream_t st, bool run) {
+  if (a.wt == DT_E4M3)
+    return a.block_m <= 16 ? ring_try<DT_E4M3, 1, G1>(a, st, run) : ring_try<DT_E4M3, 2, G1>(a, st, run);
+  return a.block_m <= 16 ? ring_try<DT_BF16, 1, G1>(a, st, run) : ring_try<DT_BF16, 2, G1>(a, st, run);
+}
+
+// Both rings need bf16 or E4M3 weights with an operand of the same type
+// (gate/up: x; down: h, which the layer keeps in the weights' type) and
+// K-dimension rows of whole 512-byte stages.
+static bool ring_rows(const GemmArgs& a, int kdim) {
+  const long long row = (long long)kdim * (a.wt == DT_BF16 ? 2 : 1);
+  return row % kRingRowBytes == 0;
 }
 
 bool gemm1_ring_applies(const GemmArgs& a) {
   if (!((a.wt == DT_BF16 && a.xt == DT_BF16) || (a.wt == DT_E4M3 && a.xt == DT_E4M3)))
     return false;
-  const long long row = (long long)a.K * (a.wt == DT_BF16 ? 2 : 1);
-  if (row % kRingRowBytes != 0 || row / kRingRowBytes < kRingD || a.N % 16 != 0) return false;
-  return (a.wt == DT_E4M3 ? g1r_dispatch<DT_E4M3>(a, nullptr, false)
-                          : g1r_dispatch<DT_BF16>(a, nullptr, false)) == 0;
+  if (!ring_rows(a, a.K) || a.N % 16 != 0 || a.M >= 255) return false;  // token rows in bytes
+  return ring_dispatch<true>(a, nullptr, false) == 0;
 }
 
-int launch_gemm1_ring(const GemmArgs& a, hipStream_t st) {
-  return a.wt == DT_E4M3 ? g1r_dispatch<DT_E4M3>(a, st, true) : g1r_dispatch<DT_BF16>(a, st, true);
-}
+int launch_gemm1_ring(const GemmArgs& a, hipStream_t st) { return ring_dispatch<true>(a, st, true); }
 
-}  // namespace moe
-
-// ===================================================== down GEMM (decode)
-//
-// Output-stationary down projection with the top-k combine fused, streaming
-// w2 through the same kind of ring.  Workgroup = 8 waves and 16 output rows
-// n0..n0+15; the stage sequence walks the active experts in id order, for
-// each expert its column passes (16*NCB tokens) and its K chunks (1 KiB of
-// each of the 16 rows = 8 K-steps, one per wave).  Each wave accumulates its
-// K-step's share for the current (expert, pass); on the pass's last chunk it
-// multiplies by scale * routing weight and adds into its own LDS accumulator
-// [M][16]; the 8 accumulators are summed in a fixed order at the end.  The
-// expert table and the per-position (token, weight) table are built in LDS
-// before the ring starts, so the steady loop issues no other memory reads
-// than the ring's and the h fragments travelling with it.
-namespace moe {
-
-constexpr int kG2RingWaves = 8;
-constexpr int kG2ChunkBytes = 1024;  // bytes of each w2 row per stage
-constexpr int kG2StageBytes = 16 * kPairStride;  // 2 halves x 8 two-row blocks
-constexpr int kG2RingMinM = 4;   // M range that takes the down-GEMM ring (measured:
-constexpr int kG2RingMaxM = 16;  // faster than the register kernel at T=8, slower at 1, 64)
-
-// (row r < 16, logical byte b < 1024) inside a down-GEMM stage
-__device__ __forceinline__ int ring2_off(int r, int b) {
-  return ((b >> 9) * 8 + (r >> 1)) * kPairStride + (r & 1) * kRingRowBytes +
-         ((b & 511) ^ ((r & 1) << 7));
-}
-
-struct G2Table {  // LDS tables of the down-GEMM ring
-  int* ek;        // [maxU] expert id
-  int* seg;       // [maxU] first sorted position
-  int* me;        // [maxU] real pairs
-  int* start;     // [maxU + 1] first stage of the expert
-  float* sc;      // [maxU] dequant scale of w2 (E4M3) times s_h, else 1
-  int* ptok;      // [cap] token of each sorted position (-1: padding)
-  float* pwt;     // [cap] routing weight of each sorted position
-};
-
-template <int WT, int OT, int NCB, int D>
-__global__ __launch_bounds__(512) void gemm2_ring_kernel(GemmArgs a, int maxU, int cap) {
-  constexpr int HT = (WT == DT_E4M3) ? DT_E4M3 : DT_BF16;
-  constexpr int NI = 2 + 2 * NCB;  // vector-memory instructions per issue
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int r16 = lane & 15, g = lane >> 4;
-  const int M = a.M, K = a.K, N = a.N;
-  const int n0 = blockIdx.x * 16;
-  constexpr int WB = Family<WT>::kBytes, HB = Family<HT>::kBytes;
-  const int nchunk = N * WB / kG2ChunkBytes;
-
-  // ---- LDS carve-up
-  char* ring = lds;
-  float* acc_lds = reinterpret_cast<float*>(lds + D * kG2StageBytes);  // [8][M][16]
-  int* ti = reinterpret_cast<int*>(acc_lds + kG2RingWaves * M * 16);
-  G2Table T;
-  T.ek = ti;
-  T.seg = T.ek + maxU;
-  T.me = T.seg + maxU;
-  T.start = T.me + maxU;
-  T.sc = reinterpret_cast<float*>(T.start + maxU + 1);
-  T.ptok = reinterpret_cast<int*>(T.sc + maxU);
-  T.pwt = reinterpret_cast<float*>(T.ptok + cap);
-  __shared__ int s_U;
-
-  // ---- tables: active experts (wave 0), per-position token/weight (all)
-  for (int i = tid; i < kG2RingWaves * M * 16; i += blockDim.x) acc_lds[i] = 0.0f;
-  const int npad = *a.num_padded;
-  for (int pos = tid; pos < npad; pos += blockDim.x) {
-    const int f = a.sorted_ids[pos];
-    const bool real = f < a.P;
-    T.ptok[pos] = real ? f / a.topk : -1;
-    T.pwt[pos] = real ? a.topk_w[f] : 0.0f;
-  }
-  if (wv == 0) {
-    int U = 0;
-    for (int base = 0; base < a.E; base += kWave) {
-      const int e = base + lane;
-      int o0 = 0, o1 = 0;
-      if (e < a.E) {
-        o0 = a.offsets[e];
-        o1 = a.offsets[e + 1];
-      }
-      const bool act = o1 > o0;
-      const uint64_t bal = __ballot(act);
-      if (act) {
-        const int k = U + __popcll(bal & lanemask_lt(lane));
-        T.ek[k] = e;
-        T.seg[k] = o0;
-        T.me[k] = o1 - o0;  // padded count; trimmed below
-      }
-      U += __popcll(bal);
-    }
-    if (lane == 0) s_U = U;
-  }
-  __syncthreads();
-  const int U = s_U;
-  // real count = padded count minus the trailing padding positions
-  for (int k = tid; k < U; k += blockDim.x) {
-    int m = T.me[k];
-    const int s0 = T.seg[k];
-    while (m > 0 && T.ptok[s0 + m - 1] < 0) --m;
-    T.me[k] = m;
-    float sc = 1.0f;
-    if (WT == DT_E4M3) sc = (*a.sh) * a.w2_scale[T.ek[k]];
-    T.sc[k] = sc;
-  }
-  __syncthreads();
-  if (wv == 0) {  // stage starts: prefix sum of npass * nchunk
-    int run = 0;
-    for (int base = 0; base < U; base += kWave) {
-      const int k = base + lane;
-      int v = 0;
-      if (k < U) v = ((T.me[k] + 16 * NCB - 1) / (16 * NCB)) * nchunk;
-      int x = v;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
-      }
-      if (k < U) T.start[k] = run + x - v;
-      run += __shfl(x, 63, kWave);
-    }
-    if (lane == 0) T.start[U] = run;
-  }
-  __syncthreads();
-  const int S = T.start[U];
-
-  // ---- per-lane DMA geometry: wave wv issues blocks 2wv, 2wv+1
-  const int lrow = lane >> 5;
-  const int lb = ((lane & 31) << 4) ^ (lrow << 7);
-  int rowo[2], dst[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int bi = 2 * wv + q, rp = bi & 7;  // block bi: half bi >> 3, row pair rp
-    rowo[q] = n0 + 2 * rp + lrow;            // w2 row within the expert
-    dst[q] = bi * kPairStride;               // block order of ring2_off
-  }
-  const int hbyte[2] = {((2 * wv) >> 3) * 512 + lb, ((2 * wv + 1) >> 3) * 512 + lb};
-  const char* w2 = reinterpret_cast<const char*>(a.w2);
-  const char* hq = reinterpret_cast<const char*>(a.hq);
-
-  // cursor over stages: expert k, pass, chunk
-  struct Cur {
-    int k, pass, chunk;
-  };
-  auto advance = [&](Cur& c) {
-    if (++c.chunk == nchunk) {
-      c.chunk = 0;
-      ++c.pass;
-      if (T.start[c.k] + (c.pass) * nchunk >= T.start[c.k + 1]) {
-        c.pass = 0;
-        ++c.k;
-      }
-    }
-  };
-
-  Raw<HT> hs[D][NCB];
-  auto issue_dma = [&](const Cur& c, int slot) {
-    const int e = T.ek[c.k];
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(w2 + ((size_t)e * K + rowo[q]) * N * WB +
-                                        (size_t)c.chunk * kG2ChunkBytes + hbyte[q]),
-          reinterpret_cast<void*>(ring + slot * kG2StageBytes + dst[q]), 16, 0, kRingAux);
-  };
-  auto h_src = [&](const Cur& c, int cb) {
-    const int col = c.pass * 16 * NCB + cb * 16 + r16;
-    const int pos = T.seg[c.k] + (col < T.me[c.k] ? col : 0);
-    return hq + (size_t)pos * N * HB + (size_t)c.chunk * kG2ChunkBytes * HB / WB +
-           (size_t)(wv * 128 + g * 32) * HB / WB;
-  };
-
-  f32x4 acc[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0, 0, 0, 0};
-  float* my = acc_lds + (size_t)wv * M * 16;
-
-  auto compute = [&](const Cur& c, int slot, const Raw<HT>* hx) {
-    const char* sb = ring + slot * kG2StageBytes;
-    const int o = ring2_off(r16, wv * 128 + g * 32);
-    Raw<WT> aw;
-    aw.q[0] = ld16(sb + o);
-    aw.q[1] = ld16(sb + o + 16);
-    const auto A = to_op<WT>(aw);
-    const int me = T.me[c.k];
-    const int ncb = min(NCB, (me - c.pass * 16 * NCB + 15) / 16);
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-      if (cb < ncb) acc[cb] = mma(A, to_op<HT>(hx[cb]), acc[cb]);
-    if (c.chunk == nchunk - 1) {  // end of this (expert, pass): flush
-      const float sc = T.sc[c.k];
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const int col = c.pass * 16 * NCB + cb * 16 + r16;
-        if (cb < ncb && col < me) {
-          const int pos = T.seg[c.k] + col;
-          const float m = sc * T.pwt[pos];
-          float* dd = my + (size_t)T.ptok[pos] * 16 + 4 * g;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dd[i] += acc[cb][i] * m;
-        }
-        acc[cb] = f32x4{0, 0, 0, 0};
-      }
-    }
-  };
-
-  Cur ci{0, 0, 0}, cc{0, 0, 0};
-  int issued = 0;
-  auto issue = [&](auto slot_c) {  // h fragments + DMA of stage `issued` into ring slot
-    constexpr int SLOT = decltype(slot_c)::value;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) hs[SLOT][cb] = load_raw<HT>(h_src(ci, cb));
-    issue_dma(ci, SLOT);
-    stage_fence();
-    advance(ci);
-    ++issued;
-  };
-  if (S >= 2 * D - 1) {
-    static_for<0, D - 1>(issue);
-    int st = 0;
-    for (; st + 2 * D - 2 < S; st += D) {
-      static_for<0, D>([&](auto slot_c) {
-        constexpr int SLOT = decltype(slot_c)::value;
-        issue(std::integral_constant<int, (SLOT + D - 1) % D>{});
-        wait_vmcnt<(D - 1) * NI>();
-        wg_barrier();
-        compute(cc, SLOT, hs[SLOT]);
-        advance(cc);
-        wg_barrier();
-      });
-    }
-    // remaining stages: those already issued sit in the ring (their h
-    // fragments are re-read below), the rest is issued one at a time
-    for (; st < S; ++st) {
-      if (st >= issued) {
-        issue_dma(ci, st % D);
-        advance(ci);
-        ++issued;
-      }
-      wait_vmcnt<0>();
-      wg_barrier();
-      Raw<HT> hx[NCB];
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) hx[cb] = load_raw<HT>(h_src(cc, cb));
-      compute(cc, st % D, hx);
-      advance(cc);
-      wg_barrier();
-    }
-  } else {
-    for (int st = 0; st < S; ++st) {
-      issue_dma(ci, 0);
-      advance(ci);
-      Raw<HT> hx[NCB];
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) hx[cb] = load_raw<HT>(h_src(cc, cb));
-      wait_vmcnt<0>();
-      wg_barrier();
-      compute(cc, 0, hx);
-      advance(cc);
-      wg_barrier();
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < M * 4; i += blockDim.x) {
-    const int t = i >> 2, q = (i & 3) * 4;
-    float v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float s = 0.0f;
-      for (int w = 0; w < kG2RingWaves; ++w) s += acc_lds[((size_t)w * M + t) * 16 + q + j];
-      v[j] = s;
-    }
-    if (OT == DT_BF16) {
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + (size_t)t * K + n0 + q) =
-          make_uint2(pack_bf16x2(v[0], v[1]),
-                     pack_bf16x2(v[2], v[3]));
-    } else {
-      st16(reinterpret_cast<float*>(a.out) + (size_t)t * K + n0 + q,
-           i32x4{__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]),
-                 __float_as_int(v[3])});
-    }
-  }
-}
-
-constexpr int kG2RingDeep = 6;  // ring depth when the LDS allows it
-
-static size_t g2r_lds(const GemmArgs& a, int maxU, int cap, int D) {
-  return (size_t)D * kG2StageBytes + (size_t)kG2RingWaves * a.M * 16 * 4 +
-         ((size_t)maxU * 5 + 1) * 4 + (size_t)cap * 8;
-}
-
-static int g2r_depth(const GemmArgs& a) {
-  const int maxU = min(a.E, a.P);
-  const int cap = a.P + maxU * (a.block_m - 1);
-  const size_t budget = 160 * 1024 - 256;
-  if (g2r_lds(a, maxU, cap, kG2RingDeep) <= budget) return kG2RingDeep;
-  if (g2r_lds(a, maxU, cap, kRingD) <= budget) return kRingD;
-  return 0;
-}
+// Below 4 tokens the down GEMM keeps the streaming kernel with the combine
+// fused (measured at 1 token: the ring plus a combine launch is 3 us slower).
+constexpr int kG2RingMinM = 4;
 
 bool gemm2_ring_applies(const GemmArgs& a) {
-  if (!(a.wt == DT_BF16 || a.wt == DT_E4M3)) return false;
-  if (a.M < kG2RingMinM || a.M > kG2RingMaxM) return false;
-  const long long row = (long long)a.N * (a.wt == DT_BF16 ? 2 : 1);
-  if (row % kG2ChunkBytes) return false;
-  return g2r_depth(a) > 0;
+  if (!(a.wt == DT_BF16 || a.wt == DT_E4M3) || !(a.ot == DT_BF16 || a.ot == DT_F32)) return false;
+  if (a.M < kG2RingMinM) return false;
+  if (!ring_rows(a, a.N) || a.K % 32 != 0) return false;
+  return ring_dispatch<false>(a, nullptr, false) == 0;
 }
 
-template <int WT, int OT, int NCB, int D>
-static int g2r_launch(const GemmArgs& a, hipStream_t st) {
-  const int maxU = min(a.E, a.P);
-  const int cap = a.P + maxU * (a.block_m - 1);
-  const size_t lds = g2r_lds(a, maxU, cap, D);
-  static size_t attr = 0;  // largest dynamic LDS size enabled so far
-  if (lds > attr) {
-    int err = (int)hipFuncSetAttribute((const void*)gemm2_ring_kernel<WT, OT, NCB, D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err) return err;
-    attr = lds;
-  }
-  hipLaunchKernelGGL((gemm2_ring_kernel<WT, OT, NCB, D>), dim3(a.K / 16), dim3(512), lds, st, a,
-                     maxU, cap);
-  return (int)hipGetLastError();
-}
-
-template <int WT, int OT, int NCB>
-static int g2r_depth_dispatch(const GemmArgs& a, hipStream_t st) {
-  return g2r_depth(a) == kG2RingDeep ? g2r_launch<WT, OT, NCB, kG2RingDeep>(a, st)
-                                     : g2r_launch<WT, OT, NCB, kRingD>(a, st);
-}
-
-int launch_gemm2_ring(const GemmArgs& a, hipStream_t st) {
-  const int ncb = min((min(a.M, kStreamMaxM) + 15) / 16, kRingNcbMax);
-#define G2R(W, O)                                                                  \
-  return ncb <= 1 ? g2r_depth_dispatch<W, O, 1>(a, st) : g2r_depth_dispatch<W, O, 2>(a, st);
-  if (a.wt == DT_E4M3) {
-    if (a.ot == DT_BF16) G2R(DT_E4M3, DT_BF16) else G2R(DT_E4M3, DT_F32)
-  }
-  if (a.ot == DT_BF16) G2R(DT_BF16, DT_BF16) else G2R(DT_BF16, DT_F32)
-#undef G2R
-}
+int launch_gemm2_ring(const GemmArgs& a, hipStream_t st) { return ring_dispatch<false>(a, st, true); }
 
 }  // namespace moe

@@ -69,9 +69,10 @@ int moe_probe_gate_up(int M, int K, int N, int E, int topk, int block_m, int max
 
 // Down product and weighted combine: out [M, K] (out_dtype) from the
 // intermediate h [cap, N] (bf16, or E4M3 codes for E4M3 weights) at the
-// pairs' sorted positions.  family 0: the decode kernels (combine fused),
-// 1: the tile kernels, whose per-pair rows go to y [cap, K] (out_dtype),
-// then the combine.
+// pairs' sorted positions.  family 0: the decode kernels (the expert ring,
+// or for f32 weights the streaming kernel with the combine fused), 1: the
+// tile kernels; the ring and the tile kernels write per-pair rows to y
+// [cap, K] (out_dtype), then the combine runs.
 int moe_probe_down(int M, int K, int N, int E, int topk, int block_m, int max_blocks, int w_dtype,
                    int out_dtype, const void* h, const void* w2, const float* w2_scale,
                    const float* sh, const float* topk_w, const int32_t* sorted_ids,
@@ -94,9 +95,9 @@ int moe_probe_down(int M, int K, int N, int E, int topk, int block_m, int max_bl
   g.y = y;
   g.out = out;
   hipStream_t st = (hipStream_t)stream;
-  if (family == 0) return moe::launch_gemm2_stream(g, st);
-  if (family == 1) {
-    int err = moe::launch_gemm2_tile(g, st);
+  if (family == 0 && !moe::gemm2_ring_applies(g)) return moe::launch_gemm2_stream(g, st);
+  if (family <= 1) {
+    int err = family == 0 ? moe::launch_gemm2_ring(g, st) : moe::launch_gemm2_tile(g, st);
     return err ? err : moe::launch_combine(g, st);
   }
   return -1;

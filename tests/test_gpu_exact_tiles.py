@@ -87,9 +87,11 @@ def test_gate_up_sums_are_exact(family, wdt, M, K, N, E, k, bm):
 
 
 DOWN = [
-    (0, torch.bfloat16, 5, 2048, 512, 8, 2, 16),     # ring down kernel (4 <= M <= 16)
-    (0, torch.bfloat16, 40, 2048, 512, 8, 2, 16),    # stream down kernel
+    (0, torch.bfloat16, 5, 2048, 512, 8, 2, 16),     # expert ring + combine
+    (0, torch.bfloat16, 40, 2048, 512, 8, 2, 32),    # ring, 32-column token groups
     (0, torch.float8_e4m3fn, 12, 2048, 1024, 8, 2, 16),
+    (0, torch.bfloat16, 2, 2048, 512, 8, 2, 16),     # stream down kernel, combine fused (M < 4)
+    (0, torch.float8_e4m3fn, 3, 2048, 1024, 8, 2, 16),
     (1, torch.bfloat16, 200, 2048, 512, 8, 2, 128),  # prefill kernel + combine, 256 x 128
     (1, torch.float8_e4m3fn, 200, 2048, 512, 8, 2, 128),
     (1, torch.bfloat16, 300, 2048, 512, 8, 2, 256),  # 256 x 256 tiles
