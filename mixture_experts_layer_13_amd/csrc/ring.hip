@@ -99,14 +99,14 @@ __device__ __forceinline__ void wg_barrier() {
 // tasks inside the stream reads only LDS and never waits on the
 // vector-memory counter the ring runs on.
 //
-// At the end of a task the four K-slices are summed by wave 0 (waves 1..3
-// leave their partial sums in a small LDS area beside the ring) while the
-// other waves already work on the next task's stages.  Gate/up writes
+// At the end of a task the four K-slices are summed by a fifth wave from
+// partial sums the streaming waves leave in a small LDS area beside the
+// ring, while they already work on the next task's stages.  Gate/up writes
 // SiLU(gate) * up to h; the down projection writes each pair's 32 output
 // features, dequantised but not yet weighted, to y, and the combine kernel
 // sums the top-k rows of every token with their routing weights.
 
-constexpr int kPRedBytesPerCb = 3 * 2 * 4 * kWave * 4;  // waves 1..3 x 2 halves x 4 regs x lanes
+constexpr int kPRedBytesPerCb = 4 * 2 * 4 * kWave * 4;  // 4 streaming waves x 2 halves x 4 regs x lanes
 
 template <int WT, int NCB, int D, bool G1>
 struct PRing {
@@ -121,7 +121,6 @@ struct PRing {
   static constexpr int TW = 5 + CPG / 4;
   static constexpr int kPad = 255;
   char* ring;
-  float* red;
   const int* tab;
   const char* w;   // expert weights [E][rows][kdim]
   const char* xb;  // operand rows + this lane's 32-byte offset within a K-step
@@ -212,12 +211,23 @@ struct PRing {
   }
 };
 
+// Workgroup = kRingWaves streaming waves (each one K-step of every stage) and
+// one epilogue wave.  The epilogue wave sums the streaming waves' partial
+// sums at the end of every task and does all the global stores, while the
+// streaming waves already load and multiply the next task's stages: their
+// loop then holds only loads, so the compiler can keep counting the loads
+// in flight (a store among them makes it wait for every outstanding load
+// before the next MFMA, which empties the ring).
+constexpr int kRingWaves = 4;
+constexpr int kRingThreads = (kRingWaves + 1) * kWave;
+
 template <int WT, int NCB, int D, int WPC, bool G1>
-__global__ __launch_bounds__(256, WPC) void ring_gemm_kernel(GemmArgs a, int GT) {
+__global__ __launch_bounds__(kRingThreads, WPC) void ring_gemm_kernel(GemmArgs a, int GT) {
   using R_t = PRing<WT, NCB, D, G1>;
   constexpr int CPG = R_t::CPG, TW = R_t::TW, WB = R_t::WB;
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int bm = a.block_m;
   // gate/up: [E][2N][K] weights, out rows N per half, K-dim K; down: [E][K][N]
@@ -233,11 +243,11 @@ __global__ __launch_bounds__(256, WPC) void ring_gemm_kernel(GemmArgs a, int GT)
   // never clamped: the host sizes GT for the longest task list
   const int ng = ntw < GT ? (int)ntw : GT;
 
-  R_t R;
-  R.ring = lds;
-  R.red = reinterpret_cast<float*>(lds + D * kG1StageBytes);
+  f32x4* red = reinterpret_cast<f32x4*>(lds + D * kG1StageBytes);
   int* tab = reinterpret_cast<int*>(lds + D * kG1StageBytes + NCB * kPRedBytesPerCb);
-  R.tab = tab;
+  // partial sums as [wave][half][cb][lane] x 4 floats: one 16-byte LDS access
+  // per accumulator
+  auto part = [&](int w2, int h2, int cb) { return red + ((w2 * 2 + h2) * NCB + cb) * kWave + lane; };
 
   // ---- task table: each task's expert, dequant scale, row block, first
   // sorted position and first K stage, then its column bytes.  The
@@ -245,7 +255,7 @@ __global__ __launch_bounds__(256, WPC) void ring_gemm_kernel(GemmArgs a, int GT)
   // together would otherwise all read the same 512-byte column of their rows
   // at the same time (measured on E4M3 gate/up weights at 32 and 64 tokens:
   // 8-9% slower when every task starts at stage 0).
-  for (int i = tid; i < ng * CPG; i += 256) {
+  for (int i = tid; i < ng * CPG; i += kRingThreads) {
     const int q = i / CPG, col = i - q * CPG;
     const long long t = w + q * G;
     const int gq = (int)(t / nrb), blk = gq / npb, lc = (gq - blk * npb) * CPG + col;
@@ -256,7 +266,7 @@ __global__ __launch_bounds__(256, WPC) void ring_gemm_kernel(GemmArgs a, int GT)
     }
     reinterpret_cast<uint8_t*>(tab + q * TW + 5)[col] = (uint8_t)b;
   }
-  for (int q = tid; q < ng; q += 256) {
+  for (int q = tid; q < ng; q += kRingThreads) {
     const long long t = w + q * G;
     const int gq = (int)(t / nrb), blk = gq / npb;
     const int e = a.block_expert[blk];
@@ -270,6 +280,93 @@ __global__ __launch_bounds__(256, WPC) void ring_gemm_kernel(GemmArgs a, int GT)
   }
   __syncthreads();
 
+  const int total = ng * ns;  // stages of this workgroup
+
+  if (wv == kRingWaves) {
+    // ---- epilogue wave: the same two barriers per stage as the streaming
+    // waves; after the second barrier of a task's last stage the partial
+    // sums are complete, and they stay untouched until the streaming waves
+    // pass the next stage's first barrier, which waits for this wave
+    float hmax = 0.0f;
+    int cq = 0, ck = 0;
+    for (int p = 0; p < total; ++p) {
+      wg_barrier();
+      wg_barrier();
+      if (++ck < ns) continue;
+      ck = 0;
+      const int* row = tab + cq * TW;
+      const float scale = __int_as_float(row[1]);
+      const int rb = row[2];
+      const size_t pos0 = (size_t)row[3];
+      const uint8_t* col8 = reinterpret_cast<const uint8_t*>(row + 5);
+      ++cq;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        f32x4 s0 = *part(0, 0, cb), s1 = *part(0, 1, cb);
+#pragma unroll
+        for (int w2 = 1; w2 < kRingWaves; ++w2) {
+          const f32x4 p0 = *part(w2, 0, cb), p1 = *part(w2, 1, cb);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            s0[i] += p0[i];
+            s1[i] += p1[i];
+          }
+        }
+        const int col = cb * 16 + r16;
+        if (col8[col] == R_t::kPad) continue;
+        float v0[4], v1[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v0[i] = s0[i] * scale;
+          v1[i] = s1[i] * scale;
+        }
+        const size_t pr = pos0 + col;
+        if constexpr (G1) {
+          const int N = a.N, n0 = 16 * rb;
+          float h[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) h[i] = silu(v0[i]) * v1[i];
+          if (a.probe) {
+            probe_store(a, pr, n0 + 4 * g, v0, v1);
+          } else if (WT == DT_E4M3) {
+            st16(reinterpret_cast<float*>(a.h) + pr * N + n0 + 4 * g,
+                 i32x4{__float_as_int(h[0]), __float_as_int(h[1]), __float_as_int(h[2]),
+                       __float_as_int(h[3])});
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hmax = fmaxf(hmax, __builtin_fabsf(h[i]));
+          } else {
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.h) + pr * N + n0 + 4 * g) =
+                make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+          }
+        } else {
+          const size_t o = pr * a.K + 32 * rb + 4 * g;  // rows 4g.. and 16 + 4g.. of the block
+          if (a.ot == DT_BF16) {
+            uint16_t* y = reinterpret_cast<uint16_t*>(a.y);
+            *reinterpret_cast<uint2*>(y + o) =
+                make_uint2(pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]));
+            *reinterpret_cast<uint2*>(y + o + 16) =
+                make_uint2(pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]));
+          } else {
+            float* y = reinterpret_cast<float*>(a.y);
+            st16(y + o, i32x4{__float_as_int(v0[0]), __float_as_int(v0[1]),
+                              __float_as_int(v0[2]), __float_as_int(v0[3])});
+            st16(y + o + 16, i32x4{__float_as_int(v1[0]), __float_as_int(v1[1]),
+                                   __float_as_int(v1[2]), __float_as_int(v1[3])});
+          }
+        }
+      }
+    }
+    if (G1 && WT == DT_E4M3) {
+      hmax = wave_max(hmax);
+      if (lane == 0 && hmax > 0.0f) atomicMax(a.hmax_bits, __float_as_uint(hmax));
+    }
+    return;
+  }
+
+  // ---- streaming waves
+  R_t R;
+  R.ring = lds;
+  R.tab = tab;
   R.w = reinterpret_cast<const char*>(G1 ? a.w13 : a.w2);
   R.xb = reinterpret_cast<const char*>(G1 ? a.x : a.hq) + g * 32;
   R.wrow = (size_t)kdim * WB;
@@ -287,118 +384,58 @@ __global__ __launch_bounds__(256, WPC) void ring_gemm_kernel(GemmArgs a, int GT)
   R.ik = 0;
   R.set_task(0);
 
-  int cq = 0, ck = 0;  // compute cursor: table row, stage within the task
-  float hmax = 0.0f;
+  int ck = 0;  // stage within the task being multiplied
   f32x4 acc0[NCB], acc1[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc0[cb] = acc1[cb] = f32x4{0, 0, 0, 0};
 
-  // end of a task: waves 1..3 leave their partial sums, wave 0 adds them to
-  // its own and stores the task's 32 x CPG block
-  auto finish = [&]() __attribute__((always_inline)) {
-    float* red = R.red;
-    if (wv > 0) {
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          red[(((((wv - 1) * 2 + 0) * NCB + cb) * 4 + i) << 6) + lane] = acc0[cb][i];
-          red[(((((wv - 1) * 2 + 1) * NCB + cb) * 4 + i) << 6) + lane] = acc1[cb][i];
-        }
-    }
-    wg_barrier();  // also the stage's closing barrier
-    if (wv == 0) {
-      const int* row = tab + cq * TW;
-      const float scale = __int_as_float(row[1]);
-      const int rb = row[2];
-      const size_t pos0 = (size_t)row[3];
-      const uint8_t* col8 = reinterpret_cast<const uint8_t*>(row + 5);
+  // Stage p uses slot p % D.  The steady loop holds only stages that refill
+  // the ring (stage p + D - 1 exists) in whole trips of D, so every slot index
+  // is static (the operand fragments live in registers) and every path
+  // through the loop issues the same loads: the compiler can then tell which
+  // fragments have landed from the explicit waits alone.  A branch between
+  // refilling and draining stages inside the loop makes it wait for all
+  // loads in flight before some MFMAs.
+  auto stage = [&](auto slot, auto refill) __attribute__((always_inline)) {
+    R.template body<decltype(slot)::value, decltype(refill)::value>(acc0, acc1, g);
+    if (++ck == ns) {  // task done: hand the partial sums to the epilogue wave
+      ck = 0;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        const int col = cb * 16 + r16;
-        const bool real = col8[col] != R_t::kPad;
-        float v0[4], v1[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float s0 = acc0[cb][i], s1 = acc1[cb][i];
-#pragma unroll
-          for (int w2 = 0; w2 < 3; ++w2) {
-            s0 += red[((((w2 * 2 + 0) * NCB + cb) * 4 + i) << 6) + lane];
-            s1 += red[((((w2 * 2 + 1) * NCB + cb) * 4 + i) << 6) + lane];
-          }
-          v0[i] = s0 * scale;
-          v1[i] = s1 * scale;
-        }
-        if (!real) continue;
-        const size_t p = pos0 + col;
-        if constexpr (G1) {
-          const int N = a.N, n0 = 16 * rb;
-          float h[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) h[i] = silu(v0[i]) * v1[i];
-          if (a.probe) {
-            probe_store(a, p, n0 + 4 * g, v0, v1);
-          } else if (WT == DT_E4M3) {
-            st16(reinterpret_cast<float*>(a.h) + p * N + n0 + 4 * g,
-                 i32x4{__float_as_int(h[0]), __float_as_int(h[1]), __float_as_int(h[2]),
-                       __float_as_int(h[3])});
-#pragma unroll
-            for (int i = 0; i < 4; ++i) hmax = fmaxf(hmax, __builtin_fabsf(h[i]));
-          } else {
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.h) + p * N + n0 + 4 * g) =
-                make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-          }
-        } else {
-          const size_t o = p * a.K + 32 * rb + 4 * g;  // rows 4g.. and 16 + 4g.. of the block
-          if (a.ot == DT_BF16) {
-            uint16_t* y = reinterpret_cast<uint16_t*>(a.y);
-            *reinterpret_cast<uint2*>(y + o) = make_uint2(pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]));
-            *reinterpret_cast<uint2*>(y + o + 16) = make_uint2(pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]));
-          } else {
-            float* y = reinterpret_cast<float*>(a.y);
-            st16(y + o, i32x4{__float_as_int(v0[0]), __float_as_int(v0[1]), __float_as_int(v0[2]),
-                              __float_as_int(v0[3])});
-            st16(y + o + 16, i32x4{__float_as_int(v1[0]), __float_as_int(v1[1]), __float_as_int(v1[2]),
-                                   __float_as_int(v1[3])});
-          }
-        }
+        *part(wv, 0, cb) = acc0[cb];
+        *part(wv, 1, cb) = acc1[cb];
+        acc0[cb] = acc1[cb] = f32x4{0, 0, 0, 0};
       }
     }
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) acc0[cb] = acc1[cb] = f32x4{0, 0, 0, 0};
-    ++cq;
+    wg_barrier();
   };
+  using Refill = std::true_type;
+  using Drain = std::false_type;
 
-  // Stage p: slot p % D, refilled with stage p + D - 1 while one remains.
-  // Whole trips of D stages keep every slot index static (the operand
-  // fragments live in registers); the tail trip checks p against the total.
-  const int total = ng * ns;
-  static_for<0, D - 1>([&](auto i) {
-    if (decltype(i)::value < total) R.template issue<decltype(i)::value>();
-  });
-  for (int st = 0; st < total; st += D) {
-    static_for<0, D>([&](auto i) __attribute__((always_inline)) {
-      constexpr int SL = decltype(i)::value;
-      const int p = st + SL;
-      if (p < total) {
-        if (p + D - 1 < total)
-          R.template body<SL, true>(acc0, acc1, g);
-        else
-          R.template body<SL, false>(acc0, acc1, g);
-        if (++ck == ns) {
-          ck = 0;
-          finish();
-        } else {
-          wg_barrier();
-        }
-      }
+  if (total < D - 1) {  // fewer stages than the ring holds: load all, then drain
+    static_for<0, D - 1>([&](auto i) {
+      if (decltype(i)::value < total) R.template issue<decltype(i)::value>();
     });
+    static_for<0, D - 1>([&](auto i) {
+      if (decltype(i)::value < total) stage(i, Drain{});
+    });
+    return;
   }
-
-  if (G1 && WT == DT_E4M3 && wv == 0) {
-    hmax = wave_max(hmax);
-    if (lane == 0 && hmax > 0.0f) atomicMax(a.hmax_bits, __float_as_uint(hmax));
-  }
+  static_for<0, D - 1>([&](auto i) { R.template issue<decltype(i)::value>(); });
+  const int n_issue = total - (D - 1);  // stages that refill the ring
+  int st = 0;
+  for (; st + D <= n_issue; st += D) static_for<0, D>([&](auto i) { stage(i, Refill{}); });
+  // the last n_issue % D refilling stages, then D - 1 draining ones
+  const int rem = n_issue - st;  // 0 .. D - 1
+  static_for<0, D>([&](auto rr) {
+    constexpr int RR = decltype(rr)::value;
+    if (rem == RR) {
+      static_for<0, RR>([&](auto i) { stage(i, Refill{}); });
+      static_for<0, D - 1>([&](auto j) {
+        stage(std::integral_constant<int, (RR + decltype(j)::value) % D>{}, Drain{});
+      });
+    }
+  });
 }
 
 // Launch: WPC workgroups per CU, the task table sized for the longest task
@@ -429,7 +466,7 @@ struct RingGemm {
       attr = bytes;
     }
     hipLaunchKernelGGL((ring_gemm_kernel<WT, NCB, D, WPC, G1>), dim3(WPC * device_cu_count()),
-                       dim3(256), bytes, st, a, table_rows(a));
+                       dim3(kRingThreads), bytes, st, a, table_rows(a));
     return (int)hipGetLastError();
   }
 };
