@@ -171,9 +171,9 @@ def main():
         peak = MFMA_PEAK_TFLOPS[wl.w_dtype]
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
-    ring = stream_path and wl.w_dtype in ("bf16", "e4m3") and (H * bw) % 512 == 0 and H * bw >= 2048
-    if stream_path:
-        roof["kernel"] = "gemm1_ring_kernel" if ring else "gemm1_stream_kernel"
+    ring = stream_path and wl.w_dtype in ("bf16", "e4m3") and (H * bw) % 512 == 0
+    if stream_path:  # the gate/up instantiation of the persistent expert ring
+        roof["kernel"] = "ring_gemm_kernel<W, NCB, 4, WPC, true>" if ring else "gemm1_stream_kernel"
     elif wl.w_dtype in ("bf16", "e4m3"):  # prefill kernels: 256 x 256 tiles with 256-row blocks
         roof["kernel"] = "pfq_gemm_kernel" if layer.block_m == 256 else "pf_gemm_kernel"
     else:
