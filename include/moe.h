@@ -150,7 +150,7 @@ moe_status moe_align_permute(const int32_t* topk_ids, int32_t M, int32_t topk,
 
 /*
  * moe_route_topk followed by moe_align_permute, with the same arguments and
- * results as the two calls (bit for bit).  When M <= 16 and M*topk <= 1024
+ * results as the two calls (bit for bit).  When M <= 8 and M*topk <= 1024
  * both run in one workgroup of one launch (one token row per wave), the ids
  * staying on chip between them; this is the small-decode case, where the
  * fixed cost of a launch is a visible part of the layer's time.  Larger

@@ -9,8 +9,9 @@
 //
 //   amax_partial_kernel: per-workgroup max |x| -> partials[g]; workgroup 0
 //     also clears the running max of |h| that the gate/up GEMM raises.
-//   quant_x_kernel: reduces the partials (or the whole tensor when launched
-//     as one workgroup), writes s_x and the E4M3 codes of x.
+//   quant_x_kernel: reduces the partials (or applies a static scale), writes
+//     s_x and the E4M3 codes of x.
+//   quant_x_one_kernel: the same for up to 1 MiB of x in one workgroup.
 //   quant_h_kernel: s_h from the running max (or a static scale), codes of
 //     the fp32 intermediate with the reciprocal multiply fl32(h * fl32(1/s_h)).
 #include "common.hpp"
@@ -40,13 +41,14 @@ __device__ __forceinline__ void load8(const void* x, size_t i, float v[8]) {
   }
 }
 
+template <int NT = kQThreads>
 __device__ __forceinline__ float block_max(float v, float* red) {
   v = wave_max(v);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) red[w] = v;
   __syncthreads();
   float r = red[0];
-  for (int i = 1; i < kQThreads / kWave; ++i) r = fmaxf(r, red[i]);
+  for (int i = 1; i < NT / kWave; ++i) r = fmaxf(r, red[i]);
   __syncthreads();
   return r;
 }
@@ -113,6 +115,55 @@ __global__ __launch_bounds__(kQThreads) void quant_x_kernel(
   }
 }
 
+// One 1024-thread workgroup: max |x|, s_x, then the codes (x is read twice,
+// the second time from L2).  Up to 32 Ki values one launch beats the
+// two-kernel path (measured on E4M3 decode steps: 8 tokens x 4096 126 -> 116
+// us against a 256-thread workgroup); from 48 Ki values on the two-kernel
+// path wins (12 and 16 tokens: 4-9 us), one CU streaming too slowly.
+constexpr int kQOneThreads = 1024;
+constexpr size_t kQOneMax = (size_t)1 << 15;  // elements
+
+template <int XT>
+__global__ __launch_bounds__(kQOneThreads) void quant_x_one_kernel(
+    const void* __restrict__ x, size_t n, uint8_t* __restrict__ xq, float* __restrict__ sx_out,
+    uint32_t* __restrict__ hmax_bits) {
+  __shared__ float red[kQOneThreads / kWave];
+  constexpr size_t kStep = (size_t)kQOneThreads * 8;
+  float m = 0.0f;
+  size_t i = (size_t)threadIdx.x * 8;
+  for (; i + 3 * kStep < n; i += 4 * kStep) {  // four loads in flight per thread
+    float v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load8<XT>(x, i + u * kStep, v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(v[u][j]));
+  }
+  for (; i < n; i += kStep) {
+    float v[8];
+    load8<XT>(x, i, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
+  }
+  m = block_max<kQOneThreads>(m, red);
+  const float s = (m == 0.0f) ? 1.0f : m / 448.0f;
+  if (threadIdx.x == 0) {
+    *sx_out = s;
+    *hmax_bits = 0u;
+  }
+  for (size_t k = (size_t)threadIdx.x * 8; k < n; k += kStep) {
+    float v[8];
+    load8<XT>(x, k, v);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(v[j] / s) << (8 * j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hi |= f32_to_e4m3(v[4 + j] / s) << (8 * j);
+    *reinterpret_cast<uint2*>(xq + k) = make_uint2(lo, hi);
+  }
+}
+
 // h32: [rows, N] fp32; codes for rows < *num_rows.
 __global__ __launch_bounds__(kQThreads) void quant_h_kernel(
     const float* __restrict__ h32, int N, const int32_t* __restrict__ num_rows,
@@ -146,9 +197,18 @@ int launch_quant_x(const void* x, int xt, size_t n, const float* static_scale,
   // n is a multiple of 128 (K % 128 == 0).
   const size_t per_wg = (size_t)kQThreads * 8;
   size_t want = (n + per_wg - 1) / per_wg;
-  if (n <= (size_t)1 << 16 || static_scale) {
-    // one workgroup reduces and quantises (small tensors), or no reduction
-    int g = static_scale ? (int)(want < 1024 ? (want ? want : 1) : 1024) : 1;
+  if (!static_scale && n <= kQOneMax) {
+    if (xt == DT_BF16)
+      hipLaunchKernelGGL(quant_x_one_kernel<DT_BF16>, dim3(1), dim3(kQOneThreads), 0, stream, x, n,
+                         xq, sx, hmax_bits);
+    else
+      hipLaunchKernelGGL(quant_x_one_kernel<DT_F32>, dim3(1), dim3(kQOneThreads), 0, stream, x, n,
+                         xq, sx, hmax_bits);
+    return (int)hipGetLastError();
+  }
+  if (static_scale) {
+    // no reduction: every workgroup quantises its part
+    int g = (int)(want < 1024 ? (want ? want : 1) : 1024);
     if (xt == DT_BF16)
       hipLaunchKernelGGL(quant_x_kernel<DT_BF16>, dim3(g), dim3(kQThreads), 0, stream,
                          x, n, partials, 0, static_scale, xq, sx, hmax_bits);

@@ -117,7 +117,7 @@ def test_align_is_deterministic():
     assert torch.equal(s1[:n], b.sorted_pair_ids[:n])
 
 
-@pytest.mark.parametrize("T,E,k,bm", [(1, 64, 8, 16), (64, 64, 8, 16), (16, 8, 2, 32), (37, 1000, 17, 64),
+@pytest.mark.parametrize("T,E,k,bm", [(1, 64, 8, 16), (8, 64, 8, 16), (64, 64, 8, 16), (16, 8, 2, 32), (37, 1000, 17, 64),
                                        (128, 256, 8, 16), (129, 64, 8, 128), (3, 2, 1, 16)])
 def test_route_align_fused_equals_separate_calls(T, E, k, bm):
     logits = inputs.make_logits(T, E, 31 + T, 1.1 if E > 8 else 0.0, device=DEV)
