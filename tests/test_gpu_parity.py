@@ -184,6 +184,8 @@ SMALL = [
     ("bf16_T65_tile", "decode_bf16", 65, 512, 256, 16, 4, 16),
     ("bf16_T200_tile", "decode_bf16", 200, 640, 384, 12, 4, 128),
     ("bf16_T300_bm256", "decode_bf16", 300, 512, 256, 8, 2, 256),
+    ("bf16_T5_K256", "decode_bf16", 5, 256, 128, 4, 2, 16),   # one 512-byte ring stage per row
+    ("fp8_T9_K512_N512", "decode_fp8", 9, 512, 512, 8, 2, 16),  # both rings one stage per task
     ("fp8_T1", "decode_fp8", 1, 512, 256, 16, 4, 16),
     ("fp8_T19", "decode_fp8", 19, 1024, 256, 16, 4, 16),
     ("fp8_T64", "decode_fp8", 64, 512, 384, 16, 8, 32),
