@@ -653,9 +653,10 @@ __global__ __launch_bounds__(256) void combine_kernel(GemmArgs a) {
 #pragma unroll
       for (int c = 0; c < Q; ++c) {
         q[j][c] = i32x4{0, 0, 0, 0};
-        if (pos[j] >= 0)
-          q[j][c] = (OT == DT_BF16) ? ld16(reinterpret_cast<const uint16_t*>(a.y) + at)
-                                    : ld16(reinterpret_cast<const float*>(a.y) + at + 4 * c);
+        if (pos[j] >= 0)  // y is read exactly once: non-temporal
+          q[j][c] = __builtin_nontemporal_load(
+              (OT == DT_BF16) ? reinterpret_cast<const i32x4*>(reinterpret_cast<const uint16_t*>(a.y) + at)
+                              : reinterpret_cast<const i32x4*>(reinterpret_cast<const float*>(a.y) + at + 4 * c));
       }
     }
 #pragma unroll
