@@ -84,8 +84,9 @@ __device__ __forceinline__ void wg_barrier() {
 // Both expert GEMMs of the decode path: one launch of a fixed number of
 // workgroups (WPC per CU) that walk a static list of tasks without draining
 // the ring between them.  Task = (column group, 32-row block): a column group
-// is 16*NCB consecutive positions of one alignment block (block_m = 16*NCB, or
-// a multiple of it, then one block is several groups), and the row block is
+// is 16*NCB consecutive sorted positions -- part of one alignment block when
+// block_m is a multiple of 16*NCB, else two consecutive 16-row blocks of one
+// expert (pair_heads) -- and the row block is
 // 32 weight rows of the block's expert -- for gate/up (G1) gate rows
 // n0..n0+15 with the matching up rows, for the down projection 32
 // consecutive rows of w2.  Tasks are numbered group-major; workgroup w takes
@@ -158,7 +159,9 @@ struct PRing {
       if constexpr (G1) {
         xrow = col8[c] == kPad ? 0 : col8[c];
       } else {
-        xrow = row[3] + c;  // padding rows of h exist (never written): their columns are dropped
+        // padding columns read the group's first row (always inside h); their
+        // sums are dropped
+        xrow = col8[c] == kPad ? row[3] : row[3] + c;
       }
       xr[cb] = xb + (size_t)xrow * wrow;
     }
@@ -211,6 +214,58 @@ struct PRing {
   }
 };
 
+constexpr int kRingWaves = 4;
+constexpr int kRingThreads = (kRingWaves + 1) * kWave;
+constexpr int kPairMaxE = 4 * kRingThreads;  // experts the pairing scan covers (4 per thread)
+
+// Alignment blocks of 16 rows and experts with more tokens than one block
+// holds: a 16-column task streams the expert's weight rows once per block.
+// Column groups of two consecutive blocks of one expert (counted from the
+// expert's first block; expert_offsets holds the padded segment starts) read
+// them once per two blocks, at the price of 32-column tasks everywhere (the
+// second block of a group may belong to the next expert, and its columns are
+// then padding).  pair_scan counts the groups, ceil(blocks / 2) per expert,
+// and gives this thread's first group index; pair_heads then writes the
+// first block of every group in group order.  wsum: kRingThreads / kWave ints
+// of LDS.  Every thread of the workgroup calls both (they synchronise it).
+__device__ __forceinline__ int pair_scan(const GemmArgs& a, int* wsum, int& my_base) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int per = (a.E + kRingThreads - 1) / kRingThreads;  // <= 4 (host check)
+  const int e0 = min(tid * per, a.E), e1 = min(e0 + per, a.E);
+  int c = 0;
+  for (int e = e0; e < e1; ++e) c += ((a.offsets[e + 1] - a.offsets[e]) / a.block_m + 1) >> 1;
+  int v = c;  // inclusive scan over the wave
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int n = __shfl_up(v, o, kWave);
+    if (lane >= o) v += n;
+  }
+  if (lane == kWave - 1) wsum[wv] = v;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < kRingThreads / kWave; ++i) {
+    const int t = wsum[i];
+    base += i < wv ? t : 0;
+    total += t;
+  }
+  my_base = base + v - c;
+  __syncthreads();  // wsum is read before anything reuses the space
+  return total;
+}
+
+__device__ __forceinline__ void pair_heads(const GemmArgs& a, int my_base, int* heads) {
+  const int tid = threadIdx.x;
+  const int per = (a.E + kRingThreads - 1) / kRingThreads;
+  const int e0 = min(tid * per, a.E), e1 = min(e0 + per, a.E);
+  int k = my_base;
+  for (int e = e0; e < e1; ++e) {
+    const int first = a.offsets[e] / a.block_m, nblk = (a.offsets[e + 1] - a.offsets[e]) / a.block_m;
+    for (int j = 0; j < nblk; j += 2) heads[k++] = first + j;
+  }
+  __syncthreads();
+}
+
 // Workgroup = kRingWaves streaming waves (each one K-step of every stage) and
 // one epilogue wave.  The epilogue wave sums the streaming waves' partial
 // sums at the end of every task and does all the global stores, while the
@@ -218,14 +273,14 @@ struct PRing {
 // loop then holds only loads, so the compiler can keep counting the loads
 // in flight (a store among them makes it wait for every outstanding load
 // before the next MFMA, which empties the ring).
-constexpr int kRingWaves = 4;
-constexpr int kRingThreads = (kRingWaves + 1) * kWave;
 
-template <int WT, int NCB, int D, int WPC, bool G1>
-__global__ __launch_bounds__(kRingThreads, WPC) void ring_gemm_kernel(GemmArgs a, int GT) {
+// heads == nullptr: column groups are blocks or parts of blocks (block_m a
+// multiple of 16 * NCB); else the ngrp groups of two 16-row blocks that
+// pair_heads listed.
+template <int WT, int NCB, int D, bool G1>
+__device__ __forceinline__ void ring_run(const GemmArgs& a, int GT, char* lds, const int* heads, int ngrp) {
   using R_t = PRing<WT, NCB, D, G1>;
   constexpr int CPG = R_t::CPG, TW = R_t::TW, WB = R_t::WB;
-  extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
@@ -236,15 +291,18 @@ __global__ __launch_bounds__(kRingThreads, WPC) void ring_gemm_kernel(GemmArgs a
   const int ns = kdim * WB / kRingRowBytes;
   const int nrb = G1 ? a.N / 16 : a.K / 32;
   const int npb = bm > CPG ? bm / CPG : 1;  // column groups per alignment block
-  const long long ntask = (long long)(*a.num_padded / bm) * npb * nrb;
+  const int nb = *a.num_padded / bm;
+  const bool span = heads != nullptr;  // groups of two blocks
+  if (!span) ngrp = nb * npb;
+
+  f32x4* red = reinterpret_cast<f32x4*>(lds + D * kG1StageBytes);
+  int* tab = reinterpret_cast<int*>(lds + D * kG1StageBytes + NCB * kPRedBytesPerCb);
+  const long long ntask = (long long)ngrp * nrb;
   const long long G = gridDim.x, w = blockIdx.x;
   const long long ntw = w < ntask ? (ntask - 1 - w) / G + 1 : 0;  // tasks w, w + G, ...
   if (ntw <= 0) return;  // uniform over the workgroup
   // never clamped: the host sizes GT for the longest task list
   const int ng = ntw < GT ? (int)ntw : GT;
-
-  f32x4* red = reinterpret_cast<f32x4*>(lds + D * kG1StageBytes);
-  int* tab = reinterpret_cast<int*>(lds + D * kG1StageBytes + NCB * kPRedBytesPerCb);
   // partial sums as [wave][half][cb][lane] x 4 floats: one 16-byte LDS access
   // per accumulator
   auto part = [&](int w2, int h2, int cb) { return red + ((w2 * 2 + h2) * NCB + cb) * kWave + lane; };
@@ -255,27 +313,40 @@ __global__ __launch_bounds__(kRingThreads, WPC) void ring_gemm_kernel(GemmArgs a
   // together would otherwise all read the same 512-byte column of their rows
   // at the same time (measured on E4M3 gate/up weights at 32 and 64 tokens:
   // 8-9% slower when every task starts at stage 0).
+  // A group's columns are the sorted positions pos0 .. pos0 + CPG - 1 with
+  // pos0 = (first block) * bm + (part of the block) * CPG; a spanning group's
+  // columns in a block of another expert, or past the last block, are padding.
   for (int i = tid; i < ng * CPG; i += kRingThreads) {
     const int q = i / CPG, col = i - q * CPG;
     const long long t = w + q * G;
-    const int gq = (int)(t / nrb), blk = gq / npb, lc = (gq - blk * npb) * CPG + col;
+    const int gq = (int)(t / nrb);
     int b = R_t::kPad;
-    if (lc < bm) {
-      const int f = a.sorted_ids[blk * bm + lc];
-      if (f < a.P) b = G1 ? f / a.topk : 0;
+    if (span) {
+      const int blk = heads[gq], bb = blk + col / bm;
+      if (bb < nb && a.block_expert[bb] == a.block_expert[blk]) {
+        const int f = a.sorted_ids[blk * bm + col];
+        if (f < a.P) b = G1 ? f / a.topk : 0;
+      }
+    } else {
+      const int blk = gq / npb, lc = (gq - blk * npb) * CPG + col;
+      if (lc < bm) {
+        const int f = a.sorted_ids[blk * bm + lc];
+        if (f < a.P) b = G1 ? f / a.topk : 0;
+      }
     }
     reinterpret_cast<uint8_t*>(tab + q * TW + 5)[col] = (uint8_t)b;
   }
   for (int q = tid; q < ng; q += kRingThreads) {
     const long long t = w + q * G;
-    const int gq = (int)(t / nrb), blk = gq / npb;
+    const int gq = (int)(t / nrb);
+    const int blk = span ? heads[gq] : gq / npb;
     const int e = a.block_expert[blk];
     float sc = 1.0f;
     if (WT == DT_E4M3) sc = G1 ? (*a.sx) * a.w13_scale[e] : (*a.sh) * a.w2_scale[e];
     tab[q * TW] = e;
     tab[q * TW + 1] = __float_as_int(sc);
     tab[q * TW + 2] = (int)(t - (long long)gq * nrb);
-    tab[q * TW + 3] = blk * bm + (gq - blk * npb) * CPG;
+    tab[q * TW + 3] = blk * bm + (span ? 0 : (gq - blk * npb) * CPG);
     tab[q * TW + 4] = (int)((((unsigned)t * 2654435761u) >> 16) % (unsigned)ns);
   }
   __syncthreads();
@@ -438,11 +509,40 @@ __global__ __launch_bounds__(kRingThreads, WPC) void ring_gemm_kernel(GemmArgs a
   });
 }
 
+// NCB = 0: 16-row alignment blocks, column groups of one or two blocks chosen
+// here from expert_offsets -- two when that removes at least an eighth of the
+// groups (the 32-column tasks cost about 2% where every expert fits one
+// block: measured on 64-token E4M3 gate/up with uniform routing).  The
+// two-block path runs a ring one stage shorter, so that both paths leave room
+// for two workgroups per CU (four stages and the partial sums of 32 columns
+// do not).
+constexpr int kPairGain = 8;
+
+template <int WT, int NCB, int D, int WPC, bool G1>
+__global__ __launch_bounds__(kRingThreads, WPC) void ring_gemm_kernel(GemmArgs a, int GT) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  if constexpr (NCB == 0) {
+    int base;
+    const int npair = pair_scan(a, reinterpret_cast<int*>(lds + D * kG1StageBytes), base);
+    const int nb = *a.num_padded / a.block_m;
+    if (kPairGain * (nb - npair) >= nb && npair < nb) {
+      // the heads sit in the ring's space, free until the first load is issued
+      int* heads = reinterpret_cast<int*>(lds);
+      pair_heads(a, base, heads);
+      ring_run<WT, 2, D - 1, G1>(a, GT, lds, heads, npair);
+    } else {
+      ring_run<WT, 1, D, G1>(a, GT, lds, nullptr, 0);
+    }
+  } else {
+    ring_run<WT, NCB, D, G1>(a, GT, lds, nullptr, 0);
+  }
+}
+
 // Launch: WPC workgroups per CU, the task table sized for the longest task
 // list a workgroup can get (capacity bound / G, rounded up, plus one).
 template <int WT, int NCB, int D, int WPC, bool G1>
 struct RingGemm {
-  using R_t = PRing<WT, NCB, D, G1>;
+  using R_t = PRing<WT, NCB == 0 ? 2 : NCB, D, G1>;  // NCB = 0: table rows of the wider groups
   static int table_rows(const GemmArgs& a) {
     const int bm = a.block_m;
     const long long npb = bm > R_t::CPG ? bm / R_t::CPG : 1;
@@ -452,8 +552,11 @@ struct RingGemm {
     return (int)((ntask + G - 1) / G) + 1;
   }
   static size_t lds(const GemmArgs& a) {
-    return (size_t)D * kG1StageBytes + NCB * kPRedBytesPerCb +
-           (size_t)table_rows(a) * R_t::TW * sizeof(int);
+    const size_t tab = (size_t)table_rows(a) * R_t::TW * sizeof(int);
+    if (NCB == 0)  // the larger of the two paths' needs
+      return max((size_t)D * kG1StageBytes + kPRedBytesPerCb + tab,
+                 (size_t)(D - 1) * kG1StageBytes + 2 * kPRedBytesPerCb + tab);
+    return (size_t)D * kG1StageBytes + NCB * kPRedBytesPerCb + tab;
   }
   static bool fits(const GemmArgs& a) { return lds(a) <= (size_t)160 * 1024 / WPC; }
   static int launch(const GemmArgs& a, hipStream_t st) {
@@ -471,8 +574,7 @@ struct RingGemm {
   }
 };
 
-// One column block per task for 16-row alignment blocks, two for wider
-// ones; two workgroups per CU (measured: one workgroup with an 8-stage ring
+// Two workgroups per CU (measured: one workgroup with an 8-stage ring
 // streams 25-40% slower), one when the task table does not leave room for
 // two.  run = false only asks whether a launch would fit (0) or not (-1).
 template <int WT, int NCB, bool G1>
@@ -484,11 +586,25 @@ static int ring_try(const GemmArgs& a, hipStream_t st, bool run) {
   return -1;
 }
 
+// 16-row alignment blocks: NCB = 0 (one- or two-block column groups, chosen
+// by the kernel) where the pairing scan covers E and the group heads fit in
+// the ring's space, else one block per group.
+constexpr bool kPairG1 = true;
+constexpr bool kPairG2 = true;
+
+static bool pair_fits(const GemmArgs& a) {
+  const long long cap = (long long)a.P + (long long)min(a.E, a.P) * (a.block_m - 1);
+  const long long nb = (cap + a.block_m - 1) / a.block_m;
+  return a.E <= kPairMaxE && nb * 4 <= (long long)(kRingD - 1) * kG1StageBytes;
+}
+
 template <bool G1>
 static int ring_dispatch(const GemmArgs& a, hipStream_t st, bool run) {
-  if (a.wt == DT_E4M3)
-    return a.block_m <= 16 ? ring_try<DT_E4M3, 1, G1>(a, st, run) : ring_try<DT_E4M3, 2, G1>(a, st, run);
-  return a.block_m <= 16 ? ring_try<DT_BF16, 1, G1>(a, st, run) : ring_try<DT_BF16, 2, G1>(a, st, run);
+  if (a.block_m > 16)
+    return a.wt == DT_E4M3 ? ring_try<DT_E4M3, 2, G1>(a, st, run) : ring_try<DT_BF16, 2, G1>(a, st, run);
+  if ((G1 ? kPairG1 : kPairG2) && pair_fits(a))
+    return a.wt == DT_E4M3 ? ring_try<DT_E4M3, 0, G1>(a, st, run) : ring_try<DT_BF16, 0, G1>(a, st, run);
+  return a.wt == DT_E4M3 ? ring_try<DT_E4M3, 1, G1>(a, st, run) : ring_try<DT_BF16, 1, G1>(a, st, run);
 }
 
 // Both rings need bf16 or E4M3 weights with an operand of the same type

@@ -186,6 +186,12 @@ SMALL = [
     ("bf16_T300_bm256", "decode_bf16", 300, 512, 256, 8, 2, 256),
     ("bf16_T5_K256", "decode_bf16", 5, 256, 128, 4, 2, 16),   # one 512-byte ring stage per row
     ("fp8_T9_K512_N512", "decode_fp8", 9, 512, 512, 8, 2, 16),  # both rings one stage per task
+    # 16-row blocks with experts of 2-4 blocks: gate/up column groups of two
+    # blocks of one expert, odd block counts, groups whose second block
+    # belongs to the next expert (uniform and Zipf routing)
+    ("bf16_T60_span", "decode_bf16", 60, 512, 256, 4, 2, 16),
+    ("bf16_T48_span_zipf", "prefill_bf16", 48, 512, 384, 8, 4, 16),
+    ("fp8_T50_span_zipf", "large_fp8", 50, 512, 256, 8, 4, 16),
     ("fp8_T1", "decode_fp8", 1, 512, 256, 16, 4, 16),
     ("fp8_T19", "decode_fp8", 19, 1024, 256, 16, 4, 16),
     ("fp8_T64", "decode_fp8", 64, 512, 384, 16, 8, 32),
