@@ -193,6 +193,9 @@ SMALL = [
     ("bf16_T48_span_zipf", "prefill_bf16", 48, 512, 384, 8, 4, 16),
     ("fp8_T50_span_zipf", "large_fp8", 50, 512, 256, 8, 4, 16),
     ("fp8_T1", "decode_fp8", 1, 512, 256, 16, 4, 16),
+    # more than 32 Ki activations: the two-launch quantisation of x (partial
+    # maxima, then s_x and the codes) ahead of the gate/up ring
+    ("fp8_T40_K1024", "decode_fp8", 40, 1024, 256, 16, 4, 16),
     ("fp8_T19", "decode_fp8", 19, 1024, 256, 16, 4, 16),
     ("fp8_T64", "decode_fp8", 64, 512, 384, 16, 8, 32),
     ("fp8_T100_tile", "decode_fp8", 100, 512, 256, 16, 4, 64),
