@@ -25,6 +25,8 @@
  *
  * What the pages leave open, and the reading taken here (each one is also
  * listed in the design notes):
+ *   - the linear router of oracle_route_project: logits = x . W_r^T with
+ *     W_r [E, K] (hidden dimension contiguous), selection on the fp64 logits;
  *   - logits are an input; selection is on the raw fp32 logits, descending,
  *     ties to the lower expert id; weights are the softmax of the logits
  *     (fp64), renormalised over the k selected when asked;
@@ -152,6 +154,64 @@ int oracle_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
     for (int j = 0; j < k; ++j) zs += exp((double)c[j].v - m);
     for (int j = 0; j < k; ++j) {
       double p = exp((double)c[j].v - m);
+      ids[t * k + j] = c[j].id;
+      w[t * k + j] = renormalize ? p / zs : p / z;
+    }
+  }
+  free(c);
+  return 0;
+}
+
+/* ------------------------------------------------------ router projection */
+
+typedef struct {
+  double v;
+  int id;
+} orc_cand64;
+
+static int cand64_cmp(const void* pa, const void* pb) {
+  const orc_cand64* a = (const orc_cand64*)pa;
+  const orc_cand64* b = (const orc_cand64*)pb;
+  if (a->v > b->v) return -1;
+  if (a->v < b->v) return 1;
+  return (a->id > b->id) - (a->id < b->id);
+}
+
+/* Token routing from the hidden states themselves.  The pages name token
+ * routing as the first stage the fused op takes over ([post], introduction;
+ * [digest], summary) but give no router formula.  Reading taken here: a
+ * linear router with one weight row per expert, stored like the expert
+ * weights with the hidden dimension contiguous (W_r [E, K]):
+ *   logits[t, e] = sum_k x[t, k] * W_r[e, k]      (fp64 over the stored values)
+ * then the selection and weights of oracle_route_topk on these fp64 logits
+ * (descending, ties to the lower id; softmax, renormalised over the k when
+ * asked).  x and W_r are f32 or bf16 (dtype codes). */
+int oracle_route_project(int x_dtype, const void* x, int w_dtype, const void* wr, int64_t T,
+                         int32_t K, int32_t E, int32_t k, int32_t renormalize, double* logits,
+                         int32_t* ids, double* w) {
+  if (T < 0 || K < 1 || E < 1 || k < 1 || k > E) return 1;
+  if ((x_dtype != ORC_F32 && x_dtype != ORC_BF16) || (w_dtype != ORC_F32 && w_dtype != ORC_BF16))
+    return 3;
+  orc_cand64* c = (orc_cand64*)malloc(sizeof(orc_cand64) * (size_t)E);
+  if (!c) return 2;
+  for (int64_t t = 0; t < T; ++t) {
+    double* l = logits + t * E;
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int32_t kk = 0; kk < K; ++kk)
+        acc += load_elem(x_dtype, x, t * K + kk) * load_elem(w_dtype, wr, (int64_t)e * K + kk);
+      l[e] = acc;
+      c[e].v = acc;
+      c[e].id = e;
+    }
+    qsort(c, (size_t)E, sizeof(orc_cand64), cand64_cmp);
+    double m = c[0].v;
+    double z = 0.0;
+    for (int e = 0; e < E; ++e) z += exp(l[e] - m);
+    double zs = 0.0;
+    for (int j = 0; j < k; ++j) zs += exp(c[j].v - m);
+    for (int j = 0; j < k; ++j) {
+      double p = exp(c[j].v - m);
       ids[t * k + j] = c[j].id;
       w[t * k + j] = renormalize ? p / zs : p / z;
     }

@@ -31,6 +31,9 @@ def lib():
         L.oracle_e4m3_from_f32.restype = ctypes.c_uint8
         L.oracle_route_topk.argtypes = [vp, c_i64, c_i32, c_i32, c_i32, vp, vp]
         L.oracle_route_topk.restype = ctypes.c_int
+        L.oracle_route_project.argtypes = [c_i32, vp, c_i32, vp, c_i64, c_i32, c_i32, c_i32,
+                                           c_i32, vp, vp, vp]
+        L.oracle_route_project.restype = ctypes.c_int
         L.oracle_align.argtypes = [vp, c_i64, c_i32, c_i32, c_i32, vp, vp, vp, vp, vp]
         L.oracle_align.restype = ctypes.c_int
         L.oracle_act_scale.argtypes = [c_i32, vp, c_i64]
@@ -81,6 +84,25 @@ def route_topk(logits, topk, renormalize=True):
     if rc:
         raise ValueError(f"oracle_route_topk failed ({rc})")
     return ids, w
+
+
+def route_project(x, wr, topk, renormalize=True):
+    """Linear router then top-k: x [T,K] and wr [E,K] (f32, or bf16 as uint16
+    bits) -> (logits f64 [T,E], ids int32 [T,k], weights f64 [T,k])."""
+    x = np.ascontiguousarray(x)
+    wr = np.ascontiguousarray(wr)
+    T, K = x.shape
+    E, K2 = wr.shape
+    if K2 != K:
+        raise ValueError("x and wr disagree on K")
+    logits = np.zeros((T, E), np.float64)
+    ids = np.zeros((T, topk), np.int32)
+    w = np.zeros((T, topk), np.float64)
+    rc = lib().oracle_route_project(_dtype_code(x), _p(x), _dtype_code(wr), _p(wr), T, K, E, topk,
+                                    int(bool(renormalize)), _p(logits), _p(ids), _p(w))
+    if rc:
+        raise ValueError(f"oracle_route_project failed ({rc})")
+    return logits, ids, w
 
 
 def align_capacity(T, topk, E, block_m):

@@ -152,6 +152,75 @@ def test_route_golden_closed_form():
     np.testing.assert_allclose(w[0], g["weights_plain"], rtol=1e-6)
 
 
+# ---------------------------------------------------------- router projection
+
+def _int_router_case(T=5, K=12, E=7, seed=3):
+    """Small integers: every product and sum is exact in fp32, bf16 and fp64."""
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-4, 5, size=(T, K)).astype(np.float32)
+    wr = rng.integers(-3, 4, size=(E, K)).astype(np.float32)
+    return x, wr
+
+
+def _bf16_bits(a32):
+    return torch.from_numpy(np.ascontiguousarray(a32, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+def test_route_project_matches_loop_bruteforce(renorm):
+    x, wr = _int_router_case()
+    T, K = x.shape
+    E = wr.shape[0]
+    # logits by explicit loops over the stored values (W_r is [E, K]: row e is expert e)
+    ref = np.zeros((T, E), np.float64)
+    for t in range(T):
+        for e in range(E):
+            ref[t, e] = sum(float(x[t, k]) * float(wr[e, k]) for k in range(K))
+    logits, ids, w = oracle.route_project(x, wr, 3, renorm)
+    assert np.array_equal(logits, ref)
+    rids, rw = bf.route(ref.astype(np.float32), 3, renorm)
+    assert np.array_equal(ids, rids)
+    np.testing.assert_allclose(w, rw, rtol=1e-13, atol=0)
+    # the same values stored as bf16 give the same result
+    l2, i2, w2 = oracle.route_project(_bf16_bits(x), _bf16_bits(wr), 3, renorm)
+    assert np.array_equal(l2, ref) and np.array_equal(i2, ids) and np.array_equal(w2, w)
+
+
+def test_route_project_closed_form_and_ties():
+    # x = 1: logit_e = K * c_e; c has a tie (1, 1) at ids 1 and 3
+    c = np.array([3, 1, 4, 1, 5, 9, 2, 6], np.float32)
+    K = 16
+    x = np.ones((2, K), np.float32)
+    wr = np.repeat(c[:, None], K, axis=1)
+    logits, ids, w = oracle.route_project(x, wr, 7, True)
+    assert np.array_equal(logits, np.tile(K * c.astype(np.float64), (2, 1)))
+    assert list(ids[0]) == [5, 7, 4, 2, 0, 6, 1]  # 9, 6, 5, 4, 3, 2, then the lower of the tied 1s
+    p = np.exp(K * (c[[5, 7, 4, 2, 0, 6, 1]].astype(np.float64) - 9))
+    np.testing.assert_allclose(w[0], p / p.sum(), rtol=1e-13)
+
+
+def test_route_project_is_linear_in_x():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((6, 64)).astype(np.float32)
+    wr = rng.standard_normal((16, 64)).astype(np.float32)
+    l1, i1, _ = oracle.route_project(x, wr, 4)
+    l2, i2, _ = oracle.route_project(2 * x, wr, 4)
+    assert np.array_equal(l2, 2 * l1) and np.array_equal(i1, i2)
+    # a transposed router (W_r read as [K, E]) would not match the product
+    np.testing.assert_allclose(l1, x.astype(np.float64) @ wr.astype(np.float64).T, rtol=1e-12, atol=1e-12)
+
+
+def test_route_project_identity_router_reduces_to_route_topk():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((9, 48)).astype(np.float32)
+    wr = np.eye(32, 48, dtype=np.float32)  # expert e reads feature e
+    logits, ids, w = oracle.route_project(x, wr, 5, False)
+    assert np.array_equal(logits, x[:, :32].astype(np.float64))
+    rids, rw = oracle.route_topk(x[:, :32], 5, False)
+    assert np.array_equal(ids, rids)
+    np.testing.assert_allclose(w, rw, rtol=1e-14)
+
+
 # ------------------------------------------------------------------ align
 
 @pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
