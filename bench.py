@@ -48,6 +48,9 @@ def parse():
                     help="tokens of the batch the CPU oracle is timed on (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="host seconds the oracle timing aims at (repeats of the sample)")
+    ap.add_argument("--router", action="store_true",
+                    help="time the router projection fused with the routing "
+                         "(moe_route_project_topk) on the workload's activations instead of the layer")
     ap.add_argument("--copy-check", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -74,12 +77,113 @@ class HipEvents:
             out.append(h.value)
         return out
 
+    def record(self, e, stream):
+        self.hip.hipEventRecord.argtypes = [self.ct.c_void_p, self.ct.c_void_p]
+        rc = self.hip.hipEventRecord(self.ct.c_void_p(e), self.ct.c_void_p(stream))
+        assert rc == 0, rc
+
     def elapsed_ms(self, a, b):
         ms = self.ct.c_float()
         rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ct.c_void_p(a),
                                           self.ct.c_void_p(b))
         assert rc == 0, rc
         return ms.value
+
+
+def router_main(args):
+    """Router projection (logits = x . W_r^T, W_r [E, H]) followed by the
+    top-k routing (moe_route_project_topk: a K-split projection launch and a
+    reduce-and-route launch), on the workload's activations and a seeded
+    router weight of the same dtype.  Algorithmic bytes: x, W_r and the ids
+    and weights (the partial sums between the two launches are not counted);
+    the kernel time is that of the whole call."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_13_amd import inputs, moe
+
+    moe.lib()  # fail loudly if the HIP library is missing
+    dev = "cuda"
+    wl = inputs.WORKLOADS[args.workload]
+    T = args.tokens
+    d = inputs.make_inputs(wl, T, device=dev)
+    H, E, k = d["H"], d["E"], d["topk"]
+    x = d["x"]
+    wr = inputs.make_router(E, H, 600 + E, x.dtype, device=dev)
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    wts = torch.empty(T, k, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(moe.moe_route_project_workspace_size(T, H, E), 16), dtype=torch.uint8,
+                     device=dev)
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        moe.moe_route_project_topk(x, wr, k, True, topk_ids=ids, topk_weights=wts, workspace=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for _ in range(K):
+                moe.moe_route_project_topk(x, wr, k, True, topk_ids=ids, topk_weights=wts, workspace=ws)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / K
+    # kernel durations: events on the launch stream around each eager call,
+    # queued behind one more replay
+    ev = HipEvents()
+    evs = ev.create(2 * K)
+    st = torch.cuda.current_stream()
+    graph.replay()
+    for i in range(K):
+        ev.record(evs[2 * i], st.cuda_stream)
+        moe.moe_route_project_topk(x, wr, k, True, topk_ids=ids, topk_weights=wts, workspace=ws)
+        ev.record(evs[2 * i + 1], st.cuda_stream)
+    torch.cuda.synchronize()
+    k_ms = sum(ev.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(K)) / K
+    b = x.element_size()
+    alg = T * H * b + E * H * b + T * k * 8
+    achieved = alg / (k_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "route_project_partial_kernel + route_project_reduce_kernel", "avg_launch_us": round(k_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": int(alg),
+            "flop_per_launch": int(2 * T * H * E)}
+    cpu = None
+    if args.cpu_sample > 0:
+        import oracle
+
+        S = min(args.cpu_sample, T)
+        xb = inputs.to_numpy_bits(x[:S])
+        wb = inputs.to_numpy_bits(wr)
+        c0 = time.perf_counter()
+        oracle.route_project(xb, wb, k, True)
+        once = time.perf_counter() - c0
+        reps = max(1, int(np.ceil(args.cpu_seconds / max(once, 1e-3))))
+        c0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.route_project(xb, wb, k, True)
+        wall = time.perf_counter() - c0
+        cpu = {"value": round(S * reps / wall, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {S} tokens of the same batch (fp64 projection and routing), "
+                         f"{reps} passes, {wall:.1f} s wall"}
+    line = {
+        "metric": "router projection + top-k routing tokens/s",
+        "value": round(T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": {torch.bfloat16: "bf16", torch.float32: "f32"}[x.dtype],
+        "data": "synthetic (seeded; no public dataset or trained weights on the pages)",
+        "config": {"workload": f"router of {args.workload} T={T} H={H} E={E} top-{k}",
+                   "tokens": T, "hidden": H, "experts": E, "topk": k},
+        "timing": "K calls captured in one HIP graph, replayed between synchronisations; "
+                  "kernel duration from HIP events around eager calls queued behind a replay",
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def main():
@@ -89,6 +193,9 @@ def main():
               "(the layer is single-GPU; see the design notes for how it would shard)",
               file=sys.stderr)
         sys.exit(2)
+    if args.router:
+        router_main(args)
+        return
     import numpy as np
     import torch
 

@@ -164,6 +164,43 @@ moe_status moe_route_align(const float* logits, int32_t M, int32_t E, int32_t to
                            size_t workspace_bytes, void* stream);
 
 /*
+ * Token routing from the hidden states: a linear router projection followed
+ * by the routing of moe_route_topk ([post], introduction, "token routing";
+ * the pages give no router formula, and this call reads it as a linear
+ * router with one weight row per expert):
+ *   logits[t, e] = sum_k x[t, k] * w_router[e, k]   (fp32 accumulation of
+ *                  bf16 products; f32 inputs are rounded to bf16 first)
+ * then ids and weights exactly as moe_route_topk computes them from these
+ * fp32 logits.  Selection follows the fp32 logits, so where two logits lie
+ * within the projection's rounding of each other the ids may differ from an
+ * exact-arithmetic router.  The projection is split over K across the chip;
+ * the slices are added in a fixed order, so the result is identical on
+ * every run.
+ * x          device [M, K] row-major, x_dtype MOE_BF16 or MOE_F32.
+ * w_router   device [E, K] row-major (the router weight transposed, like
+ *            w13 and w2: the hidden dimension contiguous), w_dtype == x_dtype.
+ * logits     device f32 [M, E] (written) or NULL.
+ * topk_ids, topk_weights: as moe_route_topk (written).
+ * workspace  device, >= moe_route_project_workspace_size() bytes, 16-byte
+ *            aligned (partial sums; no initialisation, not preserved).
+ * Limits: K a multiple of 128 in [128, 65536]; E, topk, M as moe_route_topk.
+ * x and w_router 16-byte aligned, the outputs 4-byte aligned.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE (a type other than
+ * bf16 or f32), MOE_ERR_UNSUPPORTED (x_dtype != w_dtype), MOE_ERR_ALIGN,
+ * MOE_ERR_WORKSPACE, MOE_ERR_HIP; nothing is enqueued on an error.  M == 0
+ * is a no-op.
+ */
+moe_status moe_route_project_topk(const void* x, int32_t x_dtype, const void* w_router,
+                                  int32_t w_dtype, int32_t M, int32_t K, int32_t E,
+                                  int32_t topk, int32_t renormalize, float* logits,
+                                  int32_t* topk_ids, float* topk_weights, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace moe_route_project_topk needs for M tokens, hidden size
+ * K and E experts (at most M * E * K / 32 bytes).  Host only. */
+moe_status moe_route_project_workspace_size(int32_t M, int32_t K, int32_t E, size_t* bytes);
+
+/*
  * Expert computation and weighted combine.  For each real pair (t, j) with
  * e = expert of the pair:
  *   g = x_t . w13[e, 0:N]^T,  u = x_t . w13[e, N:2N]^T,  h = SiLU(g) * u,

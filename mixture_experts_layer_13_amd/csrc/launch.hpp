@@ -11,6 +11,13 @@ namespace moe {
 
 constexpr int kMaxPartials = 1024;
 
+// Linear router projection + top-k (route_project.hip); dtype DT_BF16 or
+// DT_F32 for both x [M,K] and wr [E,K]; logits may be NULL; ws holds
+// route_project_workspace_bytes(M, K, E) bytes of partial sums.
+size_t route_project_workspace_bytes(int M, int K, int E);
+int launch_route_project(const void* x, const void* wr, int dtype, int M, int K, int E, int k,
+                         int renorm, float* logits, int32_t* ids, float* wts, void* ws,
+                         hipStream_t st);
 int launch_route_topk(const float* logits, int M, int E, int k, int renorm,
                       int32_t* ids, float* wts, hipStream_t stream);
 

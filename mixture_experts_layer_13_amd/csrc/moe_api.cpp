@@ -157,6 +157,52 @@ moe_status moe_route_topk(const float* logits, int32_t M, int32_t E, int32_t top
   return hip_status(err, "route_topk launch");
 }
 
+static moe_status check_project_dims(int32_t M, int32_t K, int32_t E) {
+  moe_status s = check_route_dims(M, E, 1);
+  if (s) return s;
+  if (K < 128 || K > 65536 || K % 128)
+    return fail(MOE_ERR_SHAPE, "K=%d must be a multiple of 128 in [128, 65536]", K);
+  return MOE_OK;
+}
+
+moe_status moe_route_project_workspace_size(int32_t M, int32_t K, int32_t E, size_t* bytes) {
+  if (!bytes) return fail(MOE_ERR_NULL, "bytes is NULL");
+  moe_status s = check_project_dims(M, K, E);
+  if (s) return s;
+  *bytes = moe::route_project_workspace_bytes(M, K, E);
+  return ok();
+}
+
+moe_status moe_route_project_topk(const void* x, int32_t x_dtype, const void* w_router,
+                                  int32_t w_dtype, int32_t M, int32_t K, int32_t E,
+                                  int32_t topk, int32_t renormalize, float* logits,
+                                  int32_t* topk_ids, float* topk_weights, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  moe_status s = check_route_dims(M, E, topk);
+  if (s) return s;
+  s = check_project_dims(M, K, E);
+  if (s) return s;
+  if ((x_dtype != MOE_BF16 && x_dtype != MOE_F32) || (w_dtype != MOE_BF16 && w_dtype != MOE_F32))
+    return fail(MOE_ERR_DTYPE, "x and router weight must be MOE_BF16 or MOE_F32");
+  if (x_dtype != w_dtype)
+    return fail(MOE_ERR_UNSUPPORTED, "x_dtype=%d and w_dtype=%d differ", x_dtype, w_dtype);
+  if (M == 0) return ok();
+  if (!x || !w_router || !topk_ids || !topk_weights || !workspace)
+    return fail(MOE_ERR_NULL, "x, w_router, topk_ids, topk_weights and workspace are required");
+  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(workspace, 16))
+    return fail(MOE_ERR_ALIGN, "x, w_router and workspace must be 16-byte aligned");
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4))
+    return fail(MOE_ERR_ALIGN, "route buffers must be 4-byte aligned");
+  const size_t need = moe::route_project_workspace_bytes(M, K, E);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  // the MOE_ dtype codes are the kernels' own (0 f32, 1 bf16)
+  int err = moe::launch_route_project(x, w_router, x_dtype, M, K, E, topk, renormalize ? 1 : 0,
+                                      logits, topk_ids, topk_weights, workspace,
+                                      (hipStream_t)stream);
+  return hip_status(err, "route_project launch");
+}
+
 moe_status moe_align_permute(const int32_t* topk_ids, int32_t M, int32_t topk, int32_t E,
                              int32_t block_m, int32_t* sorted_pair_ids,
                              int32_t* block_expert_ids, int32_t* expert_offsets,

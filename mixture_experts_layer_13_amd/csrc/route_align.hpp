@@ -29,16 +29,18 @@ __device__ __forceinline__ uint32_t float_key(float v) {
 // select on the order-preserving keys with ballots (32 bit steps, no data
 // exchange between lanes); the k winners are then ranked by (key desc, id
 // asc) with one broadcast per winner.  Must be called by a whole wave.
+// route_values: the same with the logits already in registers (lane holds
+// experts lane + 64 i in vin[i]; entries past E are ignored).
 template <int NPER>
-__device__ __forceinline__ void route_row(const float* __restrict__ l, int E, int k, int renorm,
-                                          int lane, int& out_id, float& out_w) {
+__device__ __forceinline__ void route_values(const float (&vin)[NPER], int E, int k, int renorm,
+                                             int lane, int& out_id, float& out_w) {
   float v[NPER];
   uint32_t key[NPER];
   uint64_t cur[NPER], sel[NPER];
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int e = lane + kWave * i;
-    v[i] = (e < E) ? l[e] : 0.0f;
+    v[i] = (e < E) ? vin[i] : 0.0f;
     key[i] = float_key(v[i]);
     cur[i] = __ballot(e < E);
     sel[i] = 0;
@@ -130,6 +132,18 @@ __device__ __forceinline__ void route_row(const float* __restrict__ l, int E, in
     z = wave_sum(s2);
   }
   out_w = my_p / z;
+}
+
+template <int NPER>
+__device__ __forceinline__ void route_row(const float* __restrict__ l, int E, int k, int renorm,
+                                          int lane, int& out_id, float& out_w) {
+  float v[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int e = lane + kWave * i;
+    v[i] = (e < E) ? l[e] : 0.0f;
+  }
+  route_values<NPER>(v, E, k, renorm, lane, out_id, out_w);
 }
 
 // Exclusive scan of v over a kChunk-thread workgroup; returns the prefix for

@@ -103,6 +103,14 @@ def make_x(T, H, seed, dtype, std=1.0, device="cpu"):
     return x.to(dtype).contiguous()
 
 
+def make_router(E, K, seed, dtype, device="cpu"):
+    """Router weight [E, K] (hidden dimension contiguous), N(0, 1/K): logits
+    of N(0,1) activations come out near N(0,1)."""
+    g = _gen(device, seed)
+    w = torch.randn(E, K, generator=g, device=device, dtype=torch.float32) / float(K) ** 0.5
+    return w.to(dtype).contiguous()
+
+
 def _e4m3_weights(E, R, C, seed, std, device):
     """Per expert: draw N(0, std^2) in fp32, scale = amax/448, codes by torch cast."""
     g = _gen(device, seed)

@@ -19,7 +19,8 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_align_capacity", "moe_workspace_size",
            "moe_route_topk", "moe_align_permute", "moe_fused_forward", "moe_quantize_act",
-           "moe_set_profile_events", "moe_route_align")
+           "moe_set_profile_events", "moe_route_align", "moe_route_project_topk",
+           "moe_route_project_workspace_size")
 MOE_QUANT_WORKSPACE_BYTES = 8192
 
 
@@ -66,6 +67,11 @@ def lib():
         L.moe_route_align.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                       vp, sz, vp]
         L.moe_route_align.restype = ctypes.c_int
+        L.moe_route_project_topk.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, vp, vp,
+                                             vp, vp, sz, vp]
+        L.moe_route_project_topk.restype = ctypes.c_int
+        L.moe_route_project_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+        L.moe_route_project_workspace_size.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -110,6 +116,33 @@ def moe_workspace_size(problem):
     n = ctypes.c_size_t(0)
     _check(lib().moe_workspace_size(ctypes.byref(problem), ctypes.byref(n)))
     return int(n.value)
+
+
+def moe_route_project_workspace_size(M, K, E):
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_route_project_workspace_size(M, K, E, ctypes.byref(n)))
+    return n.value
+
+
+def moe_route_project_topk(x, w_router, topk, renormalize=True, logits=None, topk_ids=None,
+                           topk_weights=None, workspace=None, stream=None):
+    """x [M,K] and w_router [E,K] (device, both bf16 or both f32) -> (ids
+    int32 [M,k], weights f32 [M,k]); logits f32 [M,E] is written if given."""
+    M, K = x.shape
+    E = w_router.shape[0]
+    if topk_ids is None:
+        topk_ids = torch.empty(M, topk, dtype=torch.int32, device=x.device)
+    if topk_weights is None:
+        topk_weights = torch.empty(M, topk, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(moe_route_project_workspace_size(M, K, E), 16),
+                                dtype=torch.uint8, device=x.device)
+    _check(lib().moe_route_project_topk(_ptr(x), dtype_code(x.dtype), _ptr(w_router),
+                                        dtype_code(w_router.dtype), M, K, E, topk,
+                                        int(bool(renormalize)), _ptr(logits), _ptr(topk_ids),
+                                        _ptr(topk_weights), _ptr(workspace), workspace.numel(),
+                                        _stream(stream)))
+    return topk_ids, topk_weights
 
 
 def moe_route_topk(logits, topk, renormalize=True, topk_ids=None, topk_weights=None,

@@ -95,6 +95,31 @@ def test_route_rejects_without_launch():
     assert L.moe_route_topk(FAKE, 0, 8, 2, 1, FAKE, FAKE, None) == moe.MOE_OK
 
 
+def test_route_project_rejects_without_launch():
+    L = moe.lib()
+    f, bf, f32 = FAKE, moe.MOE_BF16, moe.MOE_F32
+    big = 1 << 30
+
+    def call(x=f, xd=bf, w=f, wd=bf, M=4, K=256, E=8, k=2, ws=f, wsb=big):
+        return L.moe_route_project_topk(x, xd, w, wd, M, K, E, k, 1, None, f, f, ws, wsb, None)
+    assert call(x=None) == moe.MOE_ERR_NULL
+    assert call(ws=None) == moe.MOE_ERR_NULL
+    assert call(K=200) == moe.MOE_ERR_SHAPE
+    assert call(k=9) == moe.MOE_ERR_SHAPE
+    assert call(xd=2, wd=2) == moe.MOE_ERR_DTYPE
+    assert call(wd=f32) == moe.MOE_ERR_UNSUPPORTED
+    assert call(x=ctypes.c_void_p(0x7f0000001008)) == moe.MOE_ERR_ALIGN
+    assert call(wsb=0) == moe.MOE_ERR_WORKSPACE
+    assert call(M=0, ws=None, wsb=0) == moe.MOE_OK  # M == 0 launches nothing
+
+
+@pytest.mark.parametrize("M,K,E", [(1, 4096, 64), (64, 4096, 64), (8192, 4096, 64), (37, 7168, 256),
+                                   (5, 128, 1000)])
+def test_route_project_workspace_size(M, K, E):
+    n = moe.moe_route_project_workspace_size(M, K, E)
+    assert n % (M * E * 4) == 0 and M * E * 4 <= n <= M * E * 4 * (K // 128)
+
+
 def test_align_rejects_without_launch():
     L = moe.lib()
     f = FAKE
