@@ -120,6 +120,24 @@ def test_route_project_workspace_size(M, K, E):
     assert n % (M * E * 4) == 0 and M * E * 4 <= n <= M * E * 4 * (K // 128)
 
 
+def test_library_makes_no_allocation_or_synchronisation_calls():
+    """The calls allocate nothing and never wait on the device: no runtime
+    allocation, free, synchronising copy or wait appears in the library's
+    sources (kernel attributes and event records are the only other runtime
+    calls besides launches)."""
+    csrc = os.path.join(os.path.dirname(moe.__file__), "csrc")
+    banned = re.compile(r"\b(hipMalloc\w*|hipFree\w*|hipHostMalloc|hipHostFree|hipMemcpy(?!Async)\w*|"
+                        r"hipMemset(?!Async)\w*|hipDeviceSynchronize|hipStreamSynchronize|"
+                        r"hipEventSynchronize|hipStreamWaitEvent|hipModuleLoad\w*|hiprtc\w*)\s*\(")
+    hits = []
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".cpp", ".hpp")):
+            for i, line in enumerate(open(os.path.join(csrc, f)), 1):
+                if banned.search(line.split("//")[0]):
+                    hits.append(f"{f}:{i}: {line.strip()}")
+    assert not hits, hits
+
+
 def test_align_rejects_without_launch():
     L = moe.lib()
     f = FAKE
