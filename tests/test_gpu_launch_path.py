@@ -6,8 +6,8 @@ One set of buffers, sized for the largest M of the sweep, serves every M
 (views of it).  A cold pass times the first call at each new M next to the
 steady calls (no compile step: the first call costs about what later calls
 cost, a kernel family's code-object loading included).  A warm pass checks,
-per M, that the route -> align -> forward calls leave the device's free
-memory unchanged (the library allocates nothing) and that they capture into
+per M, that the route -> align -> forward calls do not lower the device's
+free memory (the library allocates nothing) and that they capture into
 a HIP graph (capture fails on any synchronisation) whose replays equal the
 eager result bit for bit.
 """
@@ -99,7 +99,9 @@ def test_launch_path_sweep(wl):
         step(M)
         torch.cuda.synchronize()
         free1 = torch.cuda.mem_get_info()[0]
-        assert free1 == free0, (M, free0, free1)
+        # an allocation would lower the free memory; it may rise when the
+        # runtime releases an earlier size's graph in the meantime
+        assert free1 >= free0, (M, free0, free1)
         eager = views(M)[4].clone()
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
