@@ -48,6 +48,8 @@ def parse():
                     help="tokens of the batch the CPU oracle is timed on (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="host seconds the oracle timing aims at (repeats of the sample)")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="single-step replays timed after flushing L2 and the MALL (0 = skip)")
     ap.add_argument("--router", action="store_true",
                     help="time the router projection fused with the routing "
                          "(moe_route_project_topk) on the workload's activations instead of the layer")
@@ -246,6 +248,32 @@ def main():
     g1_ms = sum(ev.elapsed_ms(events[4 * i], events[4 * i + 1]) for i in range(K)) / K
     g2_ms = sum(ev.elapsed_ms(events[4 * i + 2], events[4 * i + 3]) for i in range(K)) / K
 
+    # Cold cache: one step captured as a graph, replayed C times, each after
+    # a 512 MiB write that evicts the L2s and the 256 MB MALL (outside the
+    # timed region), each timed with HIP events on the launch stream.
+    C = args.cold_steps
+    cold = None
+    if C > 0:
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g1, stream=cap):
+                layer(x, logits)
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cev = ev.create(2 * C)
+        st = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        for i in range(C):
+            flush.fill_(i & 0xFF)
+            ev.record(cev[2 * i], st.cuda_stream)
+            g1.replay()
+            ev.record(cev[2 * i + 1], st.cuda_stream)
+        torch.cuda.synchronize()
+        ct = np.array([ev.elapsed_ms(cev[2 * i], cev[2 * i + 1]) for i in range(C)]) * 1e3
+        del flush, g1
+        cold = {"median_us": round(float(np.median(ct)), 2), "p10_us": round(float(np.percentile(ct, 10)), 2),
+                "p90_us": round(float(np.percentile(ct, 90)), 2), "steps": C, "flush_bytes": 512 << 20,
+                "tokens_per_s_median": round(T / (float(np.median(ct)) * 1e-6), 1)}
+
     if args.copy_check:  # plain copy of known size, for counter calibration
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -360,11 +388,15 @@ def main():
         "op_hbm_gbps": round(op_bytes / (ms_step * 1e-3) / 1e9, 1),
         "op_tflops": round(flops / (ms_step * 1e-3) / 1e12, 3),
         "down_gemm_avg_launch_us": round(g2_ms * 1e3, 2),
-        "timing": "K steps captured in one HIP graph, replayed between synchronisations; "
-                  "kernel durations from HIP events on an eager pass queued behind a replay",
+        "timing": "K steps captured in one HIP graph, replayed between synchronisations (warm: "
+                  "back to back); kernel durations from HIP events on an eager pass queued behind a "
+                  "replay; cold_cache: single-step graph replays after a 512 MiB write, HIP events",
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if cold is not None:
+        cold["op_hbm_gbps_median"] = round(op_bytes / (cold["median_us"] * 1e-6) / 1e9, 1)
+        line["cold_cache"] = cold
     print(json.dumps(line), flush=True)
 
 
