@@ -269,10 +269,18 @@ def main():
             ev.record(cev[2 * i + 1], st.cuda_stream)
         torch.cuda.synchronize()
         ct = np.array([ev.elapsed_ms(cev[2 * i], cev[2 * i + 1]) for i in range(C)]) * 1e3
+        # control: the same single-step replays without the flush
+        for i in range(C):
+            ev.record(cev[2 * i], st.cuda_stream)
+            g1.replay()
+            ev.record(cev[2 * i + 1], st.cuda_stream)
+        torch.cuda.synchronize()
+        wt = np.array([ev.elapsed_ms(cev[2 * i], cev[2 * i + 1]) for i in range(C)]) * 1e3
         del flush, g1
         cold = {"median_us": round(float(np.median(ct)), 2), "p10_us": round(float(np.percentile(ct, 10)), 2),
                 "p90_us": round(float(np.percentile(ct, 90)), 2), "steps": C, "flush_bytes": 512 << 20,
-                "tokens_per_s_median": round(T / (float(np.median(ct)) * 1e-6), 1)}
+                "tokens_per_s_median": round(T / (float(np.median(ct)) * 1e-6), 1),
+                "single_step_unflushed_median_us": round(float(np.median(wt)), 2)}
 
     if args.copy_check:  # plain copy of known size, for counter calibration
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
