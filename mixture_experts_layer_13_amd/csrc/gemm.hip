@@ -18,16 +18,21 @@
 // The post's FP8 path keeps tensor scaling, the matmul and the expert
 // aggregation in one pass over HBM ([post], "Backend routing for FP8 tensor
 // quantization"); here the dequant scales, SiLU * up and the routing weight
-// are applied to the fp32 accumulators in registers, and in the decode
-// kernels the top-k combine happens in the same kernel as the down GEMM.
+// are applied to the fp32 accumulators in registers.
 //
-// Two kernel families, chosen on the host from M:
-//   stream (M <= 64): gate/up kernel over (16-row tile, active expert) with
+// The bf16 and E4M3 decode products run on the expert rings (ring.hip) and
+// the large-batch ones on the tiles of prefill.hip / prefill2.hip.  This file
+// holds the rest, chosen on the host:
+//   stream (M <= 64 where the rings do not apply -- f32 weights, or weight
+//     rows that are not whole 512-byte ring stages -- and the down product
+//     below 4 tokens): gate/up kernel over (16-row tile, active expert) with
 //     the K loop split across 4 waves; down kernel per 16 output rows that
-//     walks every active expert and keeps the combine in LDS.
-//   tile (M > 64): one workgroup per (64-row weight tile, block_m token
-//     block of one expert); token rows staged in LDS and shared by 4 waves;
-//     down-projection rows written weighted to a buffer, then combined.
+//     walks every active expert and keeps the weighted top-k combine in LDS.
+//   tile (M > 64 with f32 weights or token blocks under 128 rows): one
+//     workgroup per (64-row weight tile, block_m token block of one expert);
+//     token rows staged in LDS and shared by 4 waves; the down-projection
+//     rows go to y, which the combine kernel sums with the routing weights.
+//   combine: out[t] = sum over the top-k slots of w[t, j] * y[pair row].
 #include "common.hpp"
 #include "launch.hpp"
 

@@ -1,5 +1,6 @@
-// ring.hip -- decode gate/up GEMM that streams expert weights through an LDS
-// ring filled by direct-to-LDS loads (gfx950 global_load_lds_dwordx4).
+// ring.hip -- the decode expert GEMMs (gate/up and down) that stream expert
+// weights through an LDS ring filled by direct-to-LDS loads (gfx950
+// global_load_lds_dwordx4).
 //
 // The expert product is A[M,K] x B[K,N] with few token rows M at decode
 // ("Amazon SageMaker AI 上的 Mixture-of-Experts 内核工程优化", section "Swap-AB
@@ -17,11 +18,12 @@
 // stay lane-ordered), which puts the 16 rows one ds_read_b128 touches on 16
 // different bank groups.
 //
-// Gate/up stage: 512 bytes of each of 32 rows (16 gate + 16 up rows of one
-// expert, 4 K-steps), one step per wave of a 4-wave workgroup.  Each wave
-// keeps its own x fragments of the kRingD - 1 stages in flight in registers,
-// issued together with the stage's DMA so that a single in-order vmcnt wait
-// covers both.
+// Stage: 512 bytes of each of 32 rows (gate/up: 16 gate + 16 up rows of one
+// expert; down: 32 consecutive rows of w2), 4 K-steps, one step per wave of
+// the 4 streaming waves.  Each wave keeps its own operand fragments (x rows
+// for gate/up, h rows for down) of the kRingD - 1 stages in flight in
+// registers, issued together with the stage's DMA so that a single in-order
+// vmcnt wait covers both.
 #include "common.hpp"
 #include "launch.hpp"
 
