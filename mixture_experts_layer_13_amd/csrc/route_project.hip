@@ -13,6 +13,9 @@
 // one K slice on v_mfma_f32_16x16x32_bf16 (router rows on the row operand,
 // tokens on the column operand, fp32 accumulation; f32 inputs are rounded to
 // bf16 on load, as the f32 expert path does) and stores its partial sums.
+// Each wave takes the whole tile over every fourth K step (x and W_r of the
+// tile are read once; with a wave per 16 experts x was read four times and
+// 8192 tokens' projection took 44.6 us instead of 28.5).
 // The second launch adds a token's slices in a fixed order (so results do
 // not depend on scheduling), keeps the logits in registers and routes them
 // with the selection and weights of moe_route_topk.  (A single launch that
@@ -26,10 +29,9 @@
 
 namespace moe {
 
-constexpr int kRpNt = 4;                // 16-token blocks per wave (one router-row load feeds 4 MFMAs)
+constexpr int kRpNt = 4;                // 16-row MFMA blocks per tile side
 constexpr int kRpTok = 16 * kRpNt;      // token rows per projection workgroup
-constexpr int kRpExp = 64;              // experts per projection workgroup (4 waves x 16)
-constexpr int kRpBatch = 4;             // MFMA steps whose loads are in flight together
+constexpr int kRpExp = 16 * kRpNt;      // experts per projection workgroup
 constexpr int kRpTargetWg = 1024;       // projection workgroups the K split aims at
 constexpr int kRpSumBatch = 8;          // partial sums loaded together by the reduction
 
@@ -74,53 +76,74 @@ __device__ __forceinline__ f32x4 rp_mma(i32x4 a, i32x4 b, f32x4 c) {
 
 // grid (blocks of 64 tokens, blocks of 64 experts, K slices of kslice
 // values): part[slice][t][e] = sum over the slice of x[t, k] * wr[e, k].
-// Wave w takes experts 16 w .. 16 w + 15 of the block for all 64 tokens.
+// Every wave computes the whole 64 x 64 tile (4 x 4 MFMA blocks: four
+// router-row loads and four token loads feed 16 MFMAs per K step) over every
+// fourth K step of the slice, so the tile's x and W_r are each read once;
+// the four waves' sums are then added in LDS in wave order.
 template <int T>
 __global__ __launch_bounds__(256) void route_project_partial_kernel(
     const void* __restrict__ x, const void* __restrict__ wr, int M, int K, int E, int kslice,
     float* __restrict__ part) {
+  __shared__ f32x4 red[3][kRpNt * kRpNt][kWave];  // waves 1-3, 48 KiB
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int s = blockIdx.z;
-  const int e0 = blockIdx.y * kRpExp + wv * 16;
-  if (e0 >= E) return;  // the wave's 16 experts all lie past E (no barrier in this kernel)
+  const int t0 = blockIdx.x * kRpTok, e0 = blockIdx.y * kRpExp;
   // rows past M or E read row 0; their sums are not stored
-  const int tok0 = blockIdx.x * kRpTok + r16, e = e0 + r16;
   const size_t k0 = (size_t)s * kslice + g * 8;
-  const size_t woff = (size_t)(e < E ? e : 0) * K + k0;
-  size_t xoff[kRpNt];
+  size_t xoff[kRpNt], woff[kRpNt];
 #pragma unroll
   for (int j = 0; j < kRpNt; ++j) {
-    const int tok = tok0 + 16 * j;
+    const int tok = t0 + 16 * j + r16, e = e0 + 16 * j + r16;
     xoff[j] = (size_t)(tok < M ? tok : 0) * K + k0;
+    woff[j] = (size_t)(e < E ? e : 0) * K + k0;
   }
-  const int nks = kslice / 32;  // a multiple of 4
-  f32x4 acc[kRpNt];
+  const int nks = kslice / 32;  // a multiple of 4: every wave takes nks / 4 steps
+  f32x4 acc[kRpNt][kRpNt];      // [token block][expert block]
 #pragma unroll
-  for (int j = 0; j < kRpNt; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int st = 0; st < nks; st += kRpBatch) {
-    i32x4 A[kRpBatch], B[kRpBatch][kRpNt];
+  for (int j = 0; j < kRpNt; ++j)
 #pragma unroll
-    for (int u = 0; u < kRpBatch; ++u) {
-      A[u] = rp_load8<T>(wr, woff + (size_t)(st + u) * 32);
+    for (int i = 0; i < kRpNt; ++i) acc[j][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int st = wv; st < nks; st += 4) {
+    i32x4 A[kRpNt], B[kRpNt];
 #pragma unroll
-      for (int j = 0; j < kRpNt; ++j) B[u][j] = rp_load8<T>(x, xoff[j] + (size_t)(st + u) * 32);
+    for (int j = 0; j < kRpNt; ++j) {
+      A[j] = rp_load8<T>(wr, woff[j] + (size_t)st * 32);
+      B[j] = rp_load8<T>(x, xoff[j] + (size_t)st * 32);
     }
 #pragma unroll
-    for (int u = 0; u < kRpBatch; ++u)
+    for (int j = 0; j < kRpNt; ++j)
 #pragma unroll
-      for (int j = 0; j < kRpNt; ++j) acc[j] = rp_mma(A[u], B[u][j], acc[j]);
+      for (int i = 0; i < kRpNt; ++i) acc[j][i] = rp_mma(A[i], B[j], acc[j][i]);
   }
-  // lane holds experts e0 + 4g + i of tokens tok0 + 16 j
+  if (wv > 0) {
+#pragma unroll
+    for (int j = 0; j < kRpNt; ++j)
+#pragma unroll
+      for (int i = 0; i < kRpNt; ++i) red[wv - 1][j * kRpNt + i][lane] = acc[j][i];
+  }
+  __syncthreads();
+  if (wv != 0) return;
+  // lane holds experts e0 + 16 i + 4g + q of tokens t0 + 16 j + r16
 #pragma unroll
   for (int j = 0; j < kRpNt; ++j) {
-    const int tok = tok0 + 16 * j;
-    if (tok < M) {
-      float* dst = part + ((size_t)s * M + tok) * E;
+    const int tok = t0 + 16 * j + r16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ee = e0 + 4 * g + i;
-        if (ee < E) dst[ee] = acc[j][i];
+    for (int i = 0; i < kRpNt; ++i) {
+      f32x4 v = acc[j][i];
+#pragma unroll
+      for (int w = 0; w < 3; ++w) {
+        const f32x4 p = red[w][j * kRpNt + i][lane];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] += p[q];
+      }
+      if (tok < M) {
+        float* dst = part + ((size_t)s * M + tok) * E;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ee = e0 + 16 * i + 4 * g + q;
+          if (ee < E) dst[ee] = v[q];
+        }
       }
     }
   }
