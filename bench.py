@@ -92,6 +92,24 @@ class HipEvents:
         return ms.value
 
 
+def read_clocks():
+    """Current shader and memory clock levels as rocm-smi reports them (a
+    child process; None where it is not available)."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                             timeout=30).stdout
+    except Exception:
+        return None
+    clk = {}
+    for ln in out.splitlines():
+        low = ln.lower()
+        for key in ("sclk", "mclk", "fclk"):
+            if f"{key} clock level" in low and "(" in ln:
+                clk[key] = ln[ln.rindex("(") + 1: ln.rindex(")")]
+    return clk or None
+
+
 def router_main(args):
     """Router projection (logits = x . W_r^T, W_r [E, H]) followed by the
     top-k routing (moe_route_project_topk: a K-split projection launch and a
@@ -282,6 +300,22 @@ def main():
                 "tokens_per_s_median": round(T / (float(np.median(ct)) * 1e-6), 1),
                 "single_step_unflushed_median_us": round(float(np.median(wt)), 2)}
 
+    # context for the roofline: a plain device-to-device copy of 1 GiB (read
+    # and write bytes counted) and the clocks the driver reports
+    ca = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cb = torch.empty_like(ca)
+    cb.copy_(ca)
+    torch.cuda.synchronize()
+    ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ce0.record()
+    for _ in range(5):
+        cb.copy_(ca)
+    ce1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * (1 << 30) / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
+    del ca, cb
+    context = {"d2d_copy_gbps": round(copy_gbps, 1), "clocks": read_clocks()}
+
     if args.copy_check:  # plain copy of known size, for counter calibration
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -405,6 +439,7 @@ def main():
     if cold is not None:
         cold["op_hbm_gbps_median"] = round(op_bytes / (cold["median_us"] * 1e-6) / 1e9, 1)
         line["cold_cache"] = cold
+    line["context"] = context
     print(json.dumps(line), flush=True)
 
 
