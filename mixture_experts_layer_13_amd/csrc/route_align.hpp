@@ -22,15 +22,14 @@ __device__ __forceinline__ uint32_t float_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Top-k of one logits row l[0:E): lanes 0..k-1 return the j-th selected id
+// Top-k of one token's logits: lanes 0..k-1 return the j-th selected id
 // (descending logit, equal values to the lower id) and its fp32 softmax
 // weight (over all E, or renormalised over the k selected).  Lane `lane`
-// holds the logits of experts lane, lane + 64, ...  Selection is a radix
-// select on the order-preserving keys with ballots (32 bit steps, no data
-// exchange between lanes); the k winners are then ranked by (key desc, id
-// asc) with one broadcast per winner.  Must be called by a whole wave.
-// route_values: the same with the logits already in registers (lane holds
-// experts lane + 64 i in vin[i]; entries past E are ignored).
+// holds the logits of experts lane, lane + 64, ... in vin[] (entries past E
+// are ignored).  Selection is a radix select on the order-preserving keys
+// with ballots (32 bit steps, no data exchange between lanes); the k winners
+// are then ranked by (key desc, id asc) with one broadcast per winner.  Must
+// be called by a whole wave.
 template <int NPER>
 __device__ __forceinline__ void route_values(const float (&vin)[NPER], int E, int k, int renorm,
                                              int lane, int& out_id, float& out_w) {
@@ -134,6 +133,7 @@ __device__ __forceinline__ void route_values(const float (&vin)[NPER], int E, in
   out_w = my_p / z;
 }
 
+// route_values on the logits row l[0:E) in memory.
 template <int NPER>
 __device__ __forceinline__ void route_row(const float* __restrict__ l, int E, int k, int renorm,
                                           int lane, int& out_id, float& out_w) {
