@@ -630,16 +630,25 @@ __global__ __launch_bounds__(256) void gemm2_tile_kernel(GemmArgs a) {
 
 // out[t] = sum over slots j (in routing order) of w[t, j] * y[pair_pos[t*k + j]]
 // (y in the output's type: bf16 or fp32; the sum in fp32).  Workgroup = one
-// token row (blockIdx.x) x 2048 columns (blockIdx.y), 8 columns per thread;
-// the slot positions and weights are wave-uniform.
+// token row (blockIdx.x) x kCombineCols columns (blockIdx.y); a thread takes
+// CG groups of 8 columns, 2048 apart (bf16: two, so that a 4096-wide row
+// fetches its slot positions and weights once and keeps 16 row loads in
+// flight per thread); the slot positions and weights are wave-uniform.
+template <int OT>
+constexpr int combine_groups() { return OT == DT_BF16 ? 2 : 1; }
+
 template <int OT>
 __global__ __launch_bounds__(256) void combine_kernel(GemmArgs a) {
+  constexpr int CG = combine_groups<OT>();
+  constexpr int Q = (OT == DT_BF16) ? 1 : 2;  // 16-byte loads per 8-column group
   const int K = a.K;
   const int t = blockIdx.x;
-  const int n = (blockIdx.y * 256 + threadIdx.x) * 8;
-  if (n >= K) return;
-  constexpr int Q = (OT == DT_BF16) ? 1 : 2;  // 16-byte loads per row slice
-  float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int nb = blockIdx.y * 2048 * CG + threadIdx.x * 8;  // group c at nb + 2048 c
+  float v[CG][8];
+#pragma unroll
+  for (int c = 0; c < CG; ++c)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[c][i] = 0.0f;
   // eight slots at a time: their rows are all requested before the first is
   // added, then added in slot order
   for (int j0 = 0; j0 < a.topk; j0 += 8) {
@@ -651,40 +660,52 @@ __global__ __launch_bounds__(256) void combine_kernel(GemmArgs a) {
       pos[j] = ok ? a.pair_pos[(size_t)t * a.topk + j0 + j] : -1;
       w[j] = ok ? a.topk_w[(size_t)t * a.topk + j0 + j] : 0.0f;
     }
-    i32x4 q[8][Q];
+    i32x4 q[8][CG][Q];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const size_t at = (size_t)(pos[j] < 0 ? 0 : pos[j]) * K + n;
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int c = 0; c < Q; ++c) {
-        q[j][c] = i32x4{0, 0, 0, 0};
-        if (pos[j] >= 0)  // y is read exactly once: non-temporal
-          q[j][c] = __builtin_nontemporal_load(
-              (OT == DT_BF16) ? reinterpret_cast<const i32x4*>(reinterpret_cast<const uint16_t*>(a.y) + at)
-                              : reinterpret_cast<const i32x4*>(reinterpret_cast<const float*>(a.y) + at + 4 * c));
+      for (int c = 0; c < CG; ++c) {
+        const int n = nb + 2048 * c;
+        const size_t at = (size_t)(pos[j] < 0 ? 0 : pos[j]) * K + n;
+#pragma unroll
+        for (int u = 0; u < Q; ++u) {
+          q[j][c][u] = i32x4{0, 0, 0, 0};
+          if (pos[j] >= 0 && n < K)  // y is read exactly once: non-temporal
+            q[j][c][u] = __builtin_nontemporal_load(
+                (OT == DT_BF16) ? reinterpret_cast<const i32x4*>(reinterpret_cast<const uint16_t*>(a.y) + at)
+                                : reinterpret_cast<const i32x4*>(reinterpret_cast<const float*>(a.y) + at + 4 * u));
+        }
       }
-    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (pos[j] < 0) continue;
-      if (OT == DT_BF16) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          v[2 * c] += w[j] * bf16_bits_to_f32((uint32_t)q[j][0][c] & 0xffffu);
-          v[2 * c + 1] += w[j] * bf16_bits_to_f32((uint32_t)q[j][0][c] >> 16);
-        }
-      } else {
+      for (int c = 0; c < CG; ++c) {
+        if (OT == DT_BF16) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          v[c] += w[j] * __int_as_float(q[j][0][c]);
-          v[4 + c] += w[j] * __int_as_float(q[j][Q - 1][c]);
+          for (int i = 0; i < 4; ++i) {
+            v[c][2 * i] += w[j] * bf16_bits_to_f32((uint32_t)q[j][c][0][i] & 0xffffu);
+            v[c][2 * i + 1] += w[j] * bf16_bits_to_f32((uint32_t)q[j][c][0][i] >> 16);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[c][i] += w[j] * __int_as_float(q[j][c][0][i]);
+            v[c][4 + i] += w[j] * __int_as_float(q[j][c][Q - 1][i]);
+          }
         }
       }
     }
   }
-  const size_t o = (size_t)t * K + n;
-  store_out4<OT>(a.out, o, v);
-  store_out4<OT>(a.out, o + 4, v + 4);
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    const int n = nb + 2048 * c;
+    if (n < K) {
+      const size_t o = (size_t)t * K + n;
+      store_out4<OT>(a.out, o, v[c]);
+      store_out4<OT>(a.out, o + 4, v[c] + 4);
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict__ src,
@@ -804,11 +825,15 @@ int launch_gemm2_tile(const GemmArgs& a, hipStream_t st) {
 }
 
 int launch_combine(const GemmArgs& a, hipStream_t st) {
-  dim3 grid((unsigned)a.M, (unsigned)((a.K + 2047) / 2048));
-  if (a.ot == DT_BF16)
-    hipLaunchKernelGGL(combine_kernel<DT_BF16>, grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(combine_kernel<DT_F32>, grid, dim3(256), 0, st, a);
+  if (a.ot == DT_BF16) {
+    const int cols = 2048 * combine_groups<DT_BF16>();
+    hipLaunchKernelGGL(combine_kernel<DT_BF16>, dim3((unsigned)a.M, (unsigned)((a.K + cols - 1) / cols)),
+                       dim3(256), 0, st, a);
+  } else {
+    const int cols = 2048 * combine_groups<DT_F32>();
+    hipLaunchKernelGGL(combine_kernel<DT_F32>, dim3((unsigned)a.M, (unsigned)((a.K + cols - 1) / cols)),
+                       dim3(256), 0, st, a);
+  }
   return (int)hipGetLastError();
 }
 
