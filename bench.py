@@ -93,20 +93,19 @@ class HipEvents:
 
 
 def read_clocks():
-    """Current shader and memory clock levels as rocm-smi reports them (a
-    child process; None where it is not available)."""
-    import subprocess
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
-                             timeout=30).stdout
-    except Exception:
-        return None
+    """Current shader and memory clock levels from the driver's sysfs tables
+    (the line the driver marks with '*'); plain file reads, no child
+    process.  None where the tables are not readable."""
+    import glob
     clk = {}
-    for ln in out.splitlines():
-        low = ln.lower()
-        for key in ("sclk", "mclk", "fclk"):
-            if f"{key} clock level" in low and "(" in ln:
-                clk[key] = ln[ln.rindex("(") + 1: ln.rindex(")")]
+    for key, fname in (("sclk", "pp_dpm_sclk"), ("mclk", "pp_dpm_mclk"), ("fclk", "pp_dpm_fclk")):
+        for path in sorted(glob.glob(f"/sys/class/drm/card*/device/{fname}")):
+            try:
+                for ln in open(path):
+                    if ln.rstrip().endswith("*"):
+                        clk.setdefault(key, ln.split(":", 1)[-1].strip(" *\n"))
+            except OSError:
+                pass
     return clk or None
 
 
