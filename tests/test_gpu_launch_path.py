@@ -88,10 +88,12 @@ def test_launch_path_sweep(wl):
     H.say("  M      first call ms   steady ms")
     for M, f, s_ in rows:
         H.say(f"  {M:5d}  {f:10.3f}  {s_:10.3f}")
-    # a compile step would cost tens of ms; the first call stays within a few
-    # steady calls (code-object loading of a kernel family included)
+    # a run-time compile costs hundreds of ms; the first call stays within a
+    # few steady calls plus the upload of a kernel family's code object (4 ms
+    # for the process's first launches on MI355X; 50 ms of margin for a cold
+    # box)
     for M, f, s_ in rows:
-        assert f < 3 * s_ + 20.0, (M, f, s_)
+        assert f < 3 * s_ + 50.0, (M, f, s_)
     # pass 2, warm: no device memory is allocated by the calls, and they
     # capture into a graph (no synchronisation) whose replays are bit-exact
     for M in SWEEP:
