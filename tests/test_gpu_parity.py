@@ -64,6 +64,8 @@ ROUTER_CASES = [
     ("bf16_T5_E1000", 5, 512, 1000, 17, torch.bfloat16),
     ("bf16_T130_E48_ksplit5", 130, 1024, 48, 6, torch.bfloat16),
     ("bf16_T300_E64", 300, 4096, 64, 8, torch.bfloat16),
+    # 64 token blocks: 16 K slices of 256, two K steps per projection wave
+    ("bf16_T4096_E64_multistep", 4096, 4096, 64, 8, torch.bfloat16),
 ]
 
 
