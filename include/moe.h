@@ -216,7 +216,7 @@ moe_status moe_route_project_workspace_size(int32_t M, int32_t K, int32_t E, siz
  *   x codes = E4M3(fl32(x / s_x)), round to nearest even, saturating;
  *   GEMM1 output scaled by s_x * w13_scale[e];
  *   s_h = a2_scale ? *a2_scale : fl32(amax|h| / 448) over all real pairs,
- *   h codes = E4M3(fl32(h * fl32(1 / s_h)));
+ *   h codes = E4M3(fl32(h / s_h)), IEEE fp32 division;
  *   GEMM2 output scaled by s_h * w2_scale[e].
  *
  * a      device [M, K] of a_dtype.       w13  device [E, 2N, K] of w_dtype.

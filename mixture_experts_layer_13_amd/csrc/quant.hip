@@ -13,7 +13,7 @@
 //     s_x and the E4M3 codes of x.
 //   quant_x_one_kernel: the same for up to 1 MiB of x in one workgroup.
 //   quant_h_kernel: s_h from the running max (or a static scale), codes of
-//     the fp32 intermediate with the reciprocal multiply fl32(h * fl32(1/s_h)).
+//     the fp32 intermediate E4M3(fl32(h / s_h)), IEEE fp32 division.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -176,7 +176,6 @@ __global__ __launch_bounds__(kQThreads) void quant_h_kernel(
     float m = __uint_as_float(*hmax_bits);
     s = (m == 0.0f) ? 1.0f : m / 448.0f;
   }
-  const float r = 1.0f / s;
   if (blockIdx.x == 0 && threadIdx.x == 0) *sh_out = s;
   const size_t n = (size_t)(*num_rows) * N;
   for (size_t i = ((size_t)blockIdx.x * kQThreads + threadIdx.x) * 8; i < n;
@@ -184,9 +183,9 @@ __global__ __launch_bounds__(kQThreads) void quant_h_kernel(
     i32x4 a = ld16(h32 + i), b = ld16(h32 + i + 4);
     uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(__int_as_float(a[j]) * r) << (8 * j);
+    for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(__int_as_float(a[j]) / s) << (8 * j);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) hi |= f32_to_e4m3(__int_as_float(b[j]) * r) << (8 * j);
+    for (int j = 0; j < 4; ++j) hi |= f32_to_e4m3(__int_as_float(b[j]) / s) << (8 * j);
     *reinterpret_cast<uint2*>(hq + i) = make_uint2(lo, hi);
   }
 }

@@ -40,8 +40,10 @@
  *   - activation scale s = fl32(amax / 448) (1 when amax = 0); the code of x
  *     is E4M3(fl32(x / s)) with an IEEE fp32 division;
  *   - the intermediate h is quantised with one dynamic scale over all real
- *     pairs: s_h = fl32(fl32(amax|h|) / 448); its code is
- *     E4M3(fl32(fl32(h) * fl32(1 / s_h))).
+ *     pairs, the same per-tensor rule as x: s_h = fl32(amax|h| / 448) with
+ *     amax taken over the fp64 values; its code is E4M3(fl32(h / s_h)), the
+ *     quotient formed in fp64 and rounded once to binary32 (the precision in
+ *     which the encoding decision is taken).
  *
  * Parity unpinned: the element-level codes of the FP8 intermediate h.  The GPU
  * holds h in fp32 after its own summation order, so an element close to a
@@ -393,15 +395,14 @@ int oracle_moe_forward(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
         double s13 = (w_dtype == ORC_E4M3) ? (double)w13_scale[e] : 1.0;
         expert_gate_up(w_dtype, w13, s13, e, H, I, xd + t * H, ta);
         for (int32_t i = 0; i < I; ++i) {
-          double v = fabs((double)(float)ta[i]);
+          double v = fabs(ta[i]);
           if (v > amax) amax = v;
         }
         free(ta);
       }
-      sh = (amax == 0.0) ? 1.0f : (float)amax / 448.0f;
+      sh = (amax == 0.0) ? 1.0f : (float)(amax / 448.0);
     }
   }
-  float rh = 1.0f / sh;
 
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t p = 0; p < np; ++p) {
@@ -414,7 +415,7 @@ int oracle_moe_forward(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
     expert_gate_up(w_dtype, w13, s13, e, H, I, xd + t * H, pa);
     if (fp8_act) {
       for (int32_t i = 0; i < I; ++i) {
-        float hv = (float)pa[i] * rh;
+        float hv = (float)(pa[i] / (double)sh);
         pa[i] = (double)sh * oracle_e4m3_to_f64(oracle_e4m3_from_f32(hv));
       }
     }

@@ -103,7 +103,8 @@ def dense_gated(x, w13, w2, ids, w):
 def fp8_forward(x_bits, w13q, w2q, s13, s2, ids, w):
     """FP8 path written with torch's E4M3 cast and numpy matmul:
     x: one dynamic scale amax/448 (fp32), codes of fl32(x / s);
-    h: one dynamic scale over all real pairs, codes of fl32(fl32(h) * fl32(1/s_h))."""
+    h: one dynamic scale fl32(amax/448) over all real pairs (amax of the fp64
+    values), codes of fl32(h / s_h) with the quotient formed in fp64."""
     x32 = decode(x_bits).astype(np.float32)
     amax = np.float32(np.abs(x32).max())
     sx = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
@@ -117,11 +118,9 @@ def fp8_forward(x_bits, w13q, w2q, s13, s2, ids, w):
         for j in range(k):
             e = ids[t, j]
             hs[t, j] = silu(w13d[e, :I] @ xd[t]) * (w13d[e, I:] @ xd[t])
-    h32 = hs.astype(np.float32)
-    hmax = np.float32(np.abs(h32).max())
-    sh = np.float32(hmax / np.float32(448.0)) if hmax > 0 else np.float32(1.0)
-    rh = np.float32(np.float32(1.0) / sh)
-    hq = e4m3_cast((h32 * rh).astype(np.float32)) * np.float64(sh)
+    hmax = np.abs(hs).max()
+    sh = np.float32(hmax / 448.0) if hmax > 0 else np.float32(1.0)
+    hq = e4m3_cast((hs / np.float64(sh)).astype(np.float32)) * np.float64(sh)
     out = np.zeros((T, w2d.shape[1]))
     for t in range(T):
         for j in range(k):

@@ -385,6 +385,34 @@ def test_forward_fp8_static_scales_are_used():
     assert (sx, sh) == (0.125, 0.5)
 
 
+def test_forward_fp8_h_code_is_the_quotient_not_a_reciprocal_product():
+    """The h code is E4M3(fl32(h / s_h)).  One token, one expert, two h
+    elements: the gate row 448 * s13 (about 100, where SiLU(g) = g exactly in
+    fp64, since exp(-100) is below half an ulp of 1) and the up row
+    0.046875 * s13, so h = 21 * s13^2 exactly.  With these s13 and static s_h
+    the exact quotient h / s_h lies strictly above 17/16, the midpoint between
+    the E4M3 values 1 and 1.125, so round-to-nearest gives 1.125 and the output
+    is 1.125 * s_h; the reciprocal product fl32(fl32(h) * fl32(1 / s_h))
+    lands exactly on the midpoint, whose tie goes to the even code 1.0."""
+    from fractions import Fraction as Fr
+
+    s13 = np.array([0x3E665517], np.uint32).view(np.float32)
+    sh = np.array([0x3F800008], np.uint32).view(np.float32)[0]
+    h = Fr(21) * Fr(float(s13[0])) ** 2
+    assert h / Fr(float(sh)) > Fr(17, 16)
+    assert np.float32(float(h) / float(sh)) > np.float32(1.0625)
+    recip = np.float32(np.float32(float(h)) * np.float32(np.float32(1.0) / sh))
+    assert recip == np.float32(1.0625)  # the other reading would round to 1.0
+    x = np.array([[1.0]], np.float32)
+    w13 = np.array([[[0x7E], [0x00], [0x14], [0x00]]], np.uint8)  # gate 448, 0; up 0.046875, 0
+    w2 = np.array([[[0x38, 0x00]]], np.uint8)  # 1, 0
+    out, (sx, s_used) = oracle.moe_forward(x, w13, w2, np.zeros((1, 1), np.int32), np.ones((1, 1)),
+                                           s13, np.ones(1, np.float32), fp8_act=True,
+                                           a1_scale=1.0, a2_scale=float(sh))
+    assert s_used == sh
+    assert out[0, 0] == 1.125 * float(sh)
+
+
 def test_pages_dimensions_golden():
     g = json.load(open(os.path.join(GOLDEN, "pages_dims.json")))
     for name in ("decode_bf16", "decode_fp8", "prefill_bf16", "prefill_fp8"):
