@@ -2,14 +2,15 @@
 
 A step is one pass of the whole layer -- route -> align -> gate/up GEMM ->
 SiLU * up -> down GEMM -> weighted combine -- over one batch of seeded
-synthetic input already resident in HBM.  Default workload: decode bf16,
-T=64 tokens, H=4096, I=1024, E=64, top-8 (1.5 GiB of expert weights, more
-than the 256 MB Infinity Cache, so every step streams its experts from HBM).
+synthetic input already resident in HBM.  Default workload: prefill bf16,
+T=8192 tokens, H=4096, I=1024, E=64, top-8 with Zipf(1.1)-skewed routing,
+the largest single-GPU configuration (the most tokens and flops);
+--workload / --tokens select the others.
 
-Prints one JSON line: tokens/s for the whole job, the roofline of the
-dominant kernel (gate/up GEMM, HIP events around each launch inside the
-timed region) and the fp64 CPU oracle timed on a bounded sample of the same
-batch on the host's cores.
+Prints one JSON line: tokens/s for the whole job (median step, each step
+after an L2/MALL flush), the roofline of the dominant kernel (the gate/up
+GEMM, HIP events around its launch inside the timed steps) and the fp64 CPU
+oracle timed on a bounded sample of the same batch on the host's cores.
 """
 import argparse
 import hashlib
@@ -24,6 +25,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 2500.0, "e4m3": 5000.0}
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "pmc_mfma.json")
 KERNEL_SRCS = [os.path.join(ROOT, "mixture_experts_layer_13_amd", "csrc", f)
                for f in ("gemm.hip", "ring.hip", "prefill.hip", "prefill2.hip", "common.hpp")]
 
@@ -40,16 +42,14 @@ def kernel_source_sha():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode_bf16")
-    ap.add_argument("--tokens", type=int, default=64)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_bf16")
+    ap.add_argument("--tokens", type=int, default=8192)
     ap.add_argument("--cpu-sample", type=int, default=64,
                     help="tokens of the batch the CPU oracle is timed on (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="host seconds the oracle timing aims at (repeats of the sample)")
-    ap.add_argument("--cold-steps", type=int, default=20,
-                    help="single-step replays timed after flushing L2 and the MALL (0 = skip)")
     ap.add_argument("--router", action="store_true",
                     help="time the router projection fused with the routing "
                          "(moe_route_project_topk) on the workload's activations instead of the layer")
@@ -232,12 +232,39 @@ def main():
 
     ev = HipEvents()
     K, W = args.steps, args.warmup
-    events = ev.create(4 * K)
+    st = torch.cuda.current_stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     for _ in range(W):
         layer(x, logits)
     torch.cuda.synchronize()
-    # The K timed steps are captured once into a HIP graph and replayed, as a
-    # serving loop would run them, so that the host does not pace the GPU.
+    # Timed region: K steps, each after a 512 MiB write that evicts the L2s
+    # and the 256 MB MALL (so every step reads its weights from HBM), each
+    # bracketed by HIP events on the launch stream, with the library's events
+    # around the two GEMM launches inside the same steps.  The host queues the
+    # next flush and step while the GPU runs, so the steps are not host-paced.
+    sev = ev.create(2 * K)
+    kev = ev.create(4 * K)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        flush.fill_(i & 0xFF)
+        ev.record(sev[2 * i], st.cuda_stream)
+        layer(x, logits, events=kev[4 * i: 4 * i + 4])
+        ev.record(sev[2 * i + 1], st.cuda_stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    step_us = np.array([ev.elapsed_ms(sev[2 * i], sev[2 * i + 1]) for i in range(K)]) * 1e3
+    g1_ms = sum(ev.elapsed_ms(kev[4 * i], kev[4 * i + 1]) for i in range(K)) / K
+    g2_ms = sum(ev.elapsed_ms(kev[4 * i + 2], kev[4 * i + 3]) for i in range(K)) / K
+    med_us = float(np.median(step_us))
+    ms_step = med_us * 1e-3
+    timed = {"median_us": round(med_us, 2), "p10_us": round(float(np.percentile(step_us, 10)), 2),
+             "p90_us": round(float(np.percentile(step_us, 90)), 2), "steps": K,
+             "flush_bytes": 512 << 20, "wall_s_incl_flushes": round(wall_s, 4)}
+
+    # Warm, for context: K steps captured once into a HIP graph and replayed
+    # back to back (as a serving loop runs them); between steps the MALL keeps
+    # the weights read last.
     graph = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
@@ -248,56 +275,13 @@ def main():
     torch.cuda.synchronize()
     graph.replay()  # untimed: the first replay uploads the graph
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    w0 = time.perf_counter()
     graph.replay()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / K
-    # Kernel durations: the same K steps issued eagerly with the library's
-    # events around the two GEMMs, queued behind one more replay so that the
-    # GPU runs them back to back (the events then bracket the kernels, not
-    # the host's launch latency).
-    graph.replay()
-    for i in range(K):
-        moe.moe_set_profile_events(events[4 * i: 4 * i + 4])
-        layer(x, logits)
-    torch.cuda.synchronize()
-    g1_ms = sum(ev.elapsed_ms(events[4 * i], events[4 * i + 1]) for i in range(K)) / K
-    g2_ms = sum(ev.elapsed_ms(events[4 * i + 2], events[4 * i + 3]) for i in range(K)) / K
-
-    # Cold cache: one step captured as a graph, replayed C times, each after
-    # a 512 MiB write that evicts the L2s and the 256 MB MALL (outside the
-    # timed region), each timed with HIP events on the launch stream.
-    C = args.cold_steps
-    cold = None
-    if C > 0:
-        g1 = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(g1, stream=cap):
-                layer(x, logits)
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        cev = ev.create(2 * C)
-        st = torch.cuda.current_stream()
-        torch.cuda.synchronize()
-        for i in range(C):
-            flush.fill_(i & 0xFF)
-            ev.record(cev[2 * i], st.cuda_stream)
-            g1.replay()
-            ev.record(cev[2 * i + 1], st.cuda_stream)
-        torch.cuda.synchronize()
-        ct = np.array([ev.elapsed_ms(cev[2 * i], cev[2 * i + 1]) for i in range(C)]) * 1e3
-        # control: the same single-step replays without the flush
-        for i in range(C):
-            ev.record(cev[2 * i], st.cuda_stream)
-            g1.replay()
-            ev.record(cev[2 * i + 1], st.cuda_stream)
-        torch.cuda.synchronize()
-        wt = np.array([ev.elapsed_ms(cev[2 * i], cev[2 * i + 1]) for i in range(C)]) * 1e3
-        del flush, g1
-        cold = {"median_us": round(float(np.median(ct)), 2), "p10_us": round(float(np.percentile(ct, 10)), 2),
-                "p90_us": round(float(np.percentile(ct, 90)), 2), "steps": C, "flush_bytes": 512 << 20,
-                "tokens_per_s_median": round(T / (float(np.median(ct)) * 1e-6), 1),
-                "single_step_unflushed_median_us": round(float(np.median(wt)), 2)}
+    warm_us = (time.perf_counter() - w0) * 1e6 / K
+    del graph, flush
+    warm = {"us_per_step": round(warm_us, 2), "tokens_per_s": round(T / (warm_us * 1e-6), 1),
+            "timing": "K steps in one HIP graph, replayed back to back between synchronisations"}
 
     # context for the roofline: a plain device-to-device copy of 1 GiB (read
     # and write bytes counted) and the clocks the driver reports
@@ -356,21 +340,31 @@ def main():
         roof["kernel"] = "gemm1_tile_kernel"
     roof["avg_launch_us"] = round(g1_ms * 1e3, 2)
     roof["algorithmic_bytes_per_launch"] = int(g1_bytes)
+    src_sha = kernel_source_sha()
+    key = f"{args.workload}:T{T}"
     if os.path.exists(PMC_FILE):
-        pmc = json.load(open(PMC_FILE))
-        src_sha = kernel_source_sha()
-        key = f"{args.workload}:T{T}"
-        rec = pmc.get(key)
+        rec = json.load(open(PMC_FILE)).get(key)
         if rec and rec.get("gemm_source_sha256") == src_sha:
             roof["traffic"] = int(rec["hbm_bytes_per_launch"])
+    if os.path.exists(MFMA_FILE):
+        # MFMA work and busy cycles of the gate/up kernel from a separate
+        # rocprofv3 --pmc pass over this same command (only while the GEMM
+        # sources are the ones the counters were taken with)
+        rec = json.load(open(MFMA_FILE)).get(key)
+        if rec and rec.get("gemm_source_sha256") == src_sha:
+            roof["mfma_counters"] = {k_: rec[k_] for k_ in (
+                "kernel", "mops_per_dispatch", "flop_per_dispatch", "mfma_busy_frac",
+                "clock_ghz", "counter_duration_us") if k_ in rec}
 
     cpu = None
     if args.cpu_sample > 0:
         import oracle
 
-        # the oracle on the first S tokens of the same batch, repeated until
-        # about --cpu-seconds of host work have been timed (one untimed pass
-        # first, which also sizes the repeat count)
+        # the oracle on the first S tokens of the same batch taken as a batch
+        # of their own (routing, and for E4M3 the dynamic per-tensor scales of
+        # x and h over these S tokens), repeated until about --cpu-seconds of
+        # host work have been timed (one untimed pass first, which also sizes
+        # the repeat count)
         S = min(args.cpu_sample, T)
         lg = logits.cpu().numpy()
         rids, rw = oracle.route_topk(lg, k, True)
@@ -388,8 +382,8 @@ def main():
 
         def oracle_pass():
             ro = oracle.route_topk(lg[:S], k, True)  # routing of the sample, timed
-            return oracle.moe_forward(xb[:S], w13, w2, remap[ro[0]], ro[1], s13, s2, fp8_act=fp8,
-                                      a2_scale=(0.05 if fp8 else None))[0]
+            return oracle.moe_forward(xb[:S], w13, w2, remap[ro[0]], ro[1], s13, s2,
+                                      fp8_act=fp8)[0]
 
         c0 = time.perf_counter()
         ref = oracle_pass()
@@ -403,9 +397,10 @@ def main():
         cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
         cpu = {"value": round(S * reps / wall, 3), "unit": "tokens/s", "cores": cores,
                "kind": "oracle",
-               "sample": f"first {S} tokens of the same batch (routing + {S}x{k} expert pairs in "
-                         f"fp64), {reps} passes, {wall:.1f} s wall"}
-        if not fp8:
+               "sample": f"first {S} tokens of the same batch as a batch of their own (routing + "
+                         f"{S}x{k} expert pairs in fp64" + (", dynamic x and h scales over them" if fp8 else "")
+                         + f"), {reps} passes, {wall:.1f} s wall"}
+        if not fp8:  # (E4M3: the sub-batch has its own h scale, so rows are not comparable)
             err = float((np.abs(got - ref).max(1) / np.abs(ref).max(1)).max())
             cpu["sample_max_row_rel_err_vs_gpu"] = float(f"{err:.3e}")
 
@@ -429,15 +424,17 @@ def main():
         "op_hbm_gbps": round(op_bytes / (ms_step * 1e-3) / 1e9, 1),
         "op_tflops": round(flops / (ms_step * 1e-3) / 1e12, 3),
         "down_gemm_avg_launch_us": round(g2_ms * 1e3, 2),
-        "timing": "K steps captured in one HIP graph, replayed between synchronisations (warm: "
-                  "back to back); kernel durations from HIP events on an eager pass queued behind a "
-                  "replay; cold_cache: single-step graph replays after a 512 MiB write, HIP events",
+        "timing": "median of K steps, each after a 512 MiB write that evicts L2 and the MALL, "
+                  "each timed with HIP events on the launch stream; GEMM durations from the "
+                  "library's events around its launches inside the same steps",
+        "timed": timed,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "warm": warm,
+        "gemm_source_sha256": src_sha[:16],
     }
-    if cold is not None:
-        cold["op_hbm_gbps_median"] = round(op_bytes / (cold["median_us"] * 1e-6) / 1e9, 1)
-        line["cold_cache"] = cold
+    warm["op_hbm_gbps"] = round(op_bytes / (warm_us * 1e-6) / 1e9, 1)
+    warm["op_tflops"] = round(flops / (warm_us * 1e-6) / 1e12, 3)
     line["context"] = context
     print(json.dumps(line), flush=True)
 

@@ -39,8 +39,9 @@
  *     failure of the calling thread.
  *   - M == 0 is valid: after the size checks the call returns MOE_OK and
  *     enqueues nothing (buffers may then be NULL), except where documented.
- *   - Calls are reentrant; concurrent calls must not share output or
- *     workspace buffers.
+ *   - Calls are reentrant and keep no state between calls (the one-time
+ *     set-up of a kernel's LDS limit per device is thread-safe); concurrent
+ *     calls must not share output or workspace buffers.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -98,6 +99,12 @@ int64_t moe_align_capacity(int32_t M, int32_t topk, int32_t E, int32_t block_m);
  * need for problem *p (one buffer serves both calls; its contents need no
  * initialisation and are not preserved between calls).  Host only. */
 moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
+
+/* After moe_fused_forward with E4M3 weights has run, the workspace holds the
+ * two per-tensor activation scales it applied, s_x then s_h, as fp32 at this
+ * byte offset (until the workspace is next used).  Read-only for callers; a
+ * diagnostic, not an input. */
+#define MOE_WORKSPACE_SCALES_OFFSET 4096
 
 /*
  * Top-k routing ([post], introduction, "token routing"; k experts per token,
@@ -261,15 +268,22 @@ moe_status moe_quantize_act(const void* x, int32_t x_dtype, int64_t n,
                             size_t workspace_bytes, void* stream);
 
 /*
- * Measurement hook.  When set, the next moe_fused_forward call on this
- * thread records events[0]/events[1] (hipEvent_t) on its stream right
- * before and after the gate/up GEMM kernel, and events[2]/events[3] around
- * the down GEMM kernel (for M <= 64 that kernel also does the combine; for
- * M > 64 the combine kernel runs after events[3]); the hook is then
- * cleared.  NULL entries are skipped.  Meant for eager (uncaptured)
- * calls.  Host only; no effect on results.
+ * moe_fused_forward with timing events: the same computation, arguments and
+ * errors, and in addition hipEventRecord of events[0] / events[1] (hipEvent_t
+ * passed as void*) on `stream` right before and after the gate/up GEMM
+ * launch, and of events[2] / events[3] around the down GEMM launch (for
+ * M <= 64 with f32 weights that launch also does the combine; otherwise the
+ * combine kernel runs after events[3]).  NULL entries, or events == NULL,
+ * are skipped.  For measuring kernel durations; no state is kept.
  */
-void moe_set_profile_events(void* const events[4]);
+moe_status moe_fused_forward_profiled(
+    const moe_problem* p, const void* a, const void* w13, const void* w2,
+    const float* w13_scale, const float* w2_scale, const float* a1_scale,
+    const float* a2_scale, const float* topk_weights,
+    const int32_t* sorted_pair_ids, const int32_t* block_expert_ids,
+    const int32_t* expert_offsets, const int32_t* pair_pos,
+    const int32_t* num_padded, void* out, void* workspace,
+    size_t workspace_bytes, void* stream, void* const events[4]);
 
 #ifdef __cplusplus
 }

@@ -99,14 +99,13 @@ int launch_align(const int32_t* ids, int M, int topk, int E, int bm,
     if (err) return err;
   }
   size_t lds = align_lds_bytes(E);
-  static bool attr_set = false;  // E = 1024 needs ~78 KiB of the 160 KiB LDS
-  if (!attr_set) {
-    int err = (int)hipFuncSetAttribute((const void*)align_scatter_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)align_lds_bytes(1024));
-    if (err) return err;
-    attr_set = true;
-  }
+  static OncePerDevice attr;  // E = 1024 needs ~78 KiB of the 160 KiB LDS
+  int err = attr.run([] {
+    return (int)hipFuncSetAttribute((const void*)align_scatter_kernel,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)align_lds_bytes(1024));
+  });
+  if (err) return err;
   hipLaunchKernelGGL(align_scatter_kernel, dim3(nch), dim3(kChunk), lds, stream,
                      ids, P, E, bm, nch, hist, sorted_ids, block_expert, offsets,
                      pair_pos, num_padded);
@@ -125,14 +124,13 @@ int launch_route_align(const float* logits, int M, int E, int k, int renorm, int
   const int nper = (E + kWave - 1) / kWave;
 #define RA_CASE(N)                                                                      \
   if (nper <= N) {                                                                      \
-    static bool attr = false;                                                           \
-    if (!attr) {                                                                        \
-      int err = (int)hipFuncSetAttribute((const void*)route_align_kernel<N>,            \
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,    \
-                                         (int)(kChunk * 4 + align_lds_bytes(1024)));    \
-      if (err) return err;                                                              \
-      attr = true;                                                                      \
-    }                                                                                   \
+    static OncePerDevice attr;                                                          \
+    int err = attr.run([] {                                                             \
+      return (int)hipFuncSetAttribute((const void*)route_align_kernel<N>,               \
+                                      hipFuncAttributeMaxDynamicSharedMemorySize,       \
+                                      (int)(kChunk * 4 + align_lds_bytes(1024)));       \
+    });                                                                                 \
+    if (err) return err;                                                                \
     hipLaunchKernelGGL(route_align_kernel<N>, dim3(1), dim3(kChunk), lds, stream, logits, \
                        M, E, k, renorm, bm, ids, wts, sorted_ids, block_expert, offsets, \
                        pair_pos, num_padded);                                           \

@@ -720,15 +720,20 @@ __global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict_
 // ------------------------------------------------------------------ launch
 
 int device_cu_count() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+  // the first caller on a device queries it; a concurrent first call stores
+  // the same value
+  static std::atomic<int> cus[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  int c = cus[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cus = n;
+    cus[dev].store(n, std::memory_order_relaxed);
+    c = n;
   }
-  return cus;
+  return c;
 }
 
 template <int WT, int XT>

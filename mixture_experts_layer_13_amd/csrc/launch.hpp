@@ -7,7 +7,29 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 namespace moe {
+
+constexpr int kMaxDevices = 64;
+
+// Thread-safe one-time set-up per device (kernel attributes such as the
+// dynamic LDS limit): the first caller on a device runs f, which returns 0 or
+// a hipError_t, and every caller on that device gets that result.  Declare one
+// function-local static instance per set-up site.
+struct OncePerDevice {
+  std::once_flag flag[kMaxDevices];
+  std::atomic<int> result[kMaxDevices];
+  template <class F>
+  int run(F&& f) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+      return (int)hipErrorInvalidDevice;
+    std::call_once(flag[dev], [&] { result[dev].store(f()); });
+    return result[dev].load();
+  }
+};
 
 constexpr int kMaxPartials = 1024;
 
@@ -97,7 +119,7 @@ int launch_gemm2_tile(const GemmArgs& a, hipStream_t stream);
 int launch_combine(const GemmArgs& a, hipStream_t stream);
 int launch_cast_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t stream);
 
-// Compute units of the current device (queried once).
+// Compute units of the current device (queried once per device).
 int device_cu_count();
 
 // Largest M served by the streaming (decode) kernels.

@@ -13,7 +13,6 @@
 namespace {
 
 thread_local char g_err[512] = "";
-thread_local void* g_prof[4] = {nullptr, nullptr, nullptr, nullptr};
 
 moe_status fail(moe_status s, const char* fmt, ...) {
   va_list ap;
@@ -59,6 +58,11 @@ struct Layout {
 };
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// s_x and s_h sit right after the amax partials, where the header says
+static_assert(((moe::kMaxPartials * sizeof(float) + 255) & ~(size_t)255) ==
+                  MOE_WORKSPACE_SCALES_OFFSET,
+              "scales offset");
 
 Layout layout_of(const moe_problem& p) {
   Layout L{};
@@ -265,13 +269,18 @@ moe_status moe_route_align(const float* logits, int32_t M, int32_t E, int32_t to
   return hip_status(err, "route_align launch");
 }
 
-moe_status moe_fused_forward(const moe_problem* p, const void* a, const void* w13,
-                             const void* w2, const float* w13_scale, const float* w2_scale,
-                             const float* a1_scale, const float* a2_scale,
-                             const float* topk_weights, const int32_t* sorted_pair_ids,
-                             const int32_t* block_expert_ids, const int32_t* expert_offsets,
-                             const int32_t* pair_pos, const int32_t* num_padded, void* out,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_fused_forward with optional events around the two GEMM launches.
+moe_status fused_forward(const moe_problem* p, const void* a, const void* w13, const void* w2,
+                         const float* w13_scale, const float* w2_scale, const float* a1_scale,
+                         const float* a2_scale, const float* topk_weights,
+                         const int32_t* sorted_pair_ids, const int32_t* block_expert_ids,
+                         const int32_t* expert_offsets, const int32_t* pair_pos,
+                         const int32_t* num_padded, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream, void* const* events) {
   moe_status s = check_problem(p);
   if (s) return s;
   if (p->M == 0) return ok();
@@ -358,10 +367,7 @@ moe_status moe_fused_forward(const moe_problem* p, const void* a, const void* w1
   }
 
   void* prof[4];
-  for (int i = 0; i < 4; ++i) {
-    prof[i] = g_prof[i];
-    g_prof[i] = nullptr;
-  }
+  for (int i = 0; i < 4; ++i) prof[i] = events ? events[i] : nullptr;
   if (prof[0]) (void)hipEventRecord((hipEvent_t)prof[0], st);
   err = stream_path ? moe::launch_gemm1_stream(g, st) : moe::launch_gemm1_tile(g, st);
   if (err) return hip_status(err, "gate/up GEMM launch");
@@ -392,8 +398,31 @@ moe_status moe_fused_forward(const moe_problem* p, const void* a, const void* w1
   return ok();
 }
 
-void moe_set_profile_events(void* const events[4]) {
-  for (int i = 0; i < 4; ++i) g_prof[i] = events ? events[i] : nullptr;
+}  // namespace
+
+extern "C" {
+
+moe_status moe_fused_forward(const moe_problem* p, const void* a, const void* w13,
+                             const void* w2, const float* w13_scale, const float* w2_scale,
+                             const float* a1_scale, const float* a2_scale,
+                             const float* topk_weights, const int32_t* sorted_pair_ids,
+                             const int32_t* block_expert_ids, const int32_t* expert_offsets,
+                             const int32_t* pair_pos, const int32_t* num_padded, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return fused_forward(p, a, w13, w2, w13_scale, w2_scale, a1_scale, a2_scale, topk_weights,
+                       sorted_pair_ids, block_expert_ids, expert_offsets, pair_pos, num_padded,
+                       out, workspace, workspace_bytes, stream, nullptr);
+}
+
+moe_status moe_fused_forward_profiled(
+    const moe_problem* p, const void* a, const void* w13, const void* w2,
+    const float* w13_scale, const float* w2_scale, const float* a1_scale, const float* a2_scale,
+    const float* topk_weights, const int32_t* sorted_pair_ids, const int32_t* block_expert_ids,
+    const int32_t* expert_offsets, const int32_t* pair_pos, const int32_t* num_padded, void* out,
+    void* workspace, size_t workspace_bytes, void* stream, void* const events[4]) {
+  return fused_forward(p, a, w13, w2, w13_scale, w2_scale, a1_scale, a2_scale, topk_weights,
+                       sorted_pair_ids, block_expert_ids, expert_offsets, pair_pos, num_padded,
+                       out, workspace, workspace_bytes, stream, events);
 }
 
 moe_status moe_quantize_act(const void* x, int32_t x_dtype, int64_t n, const float* static_scale,

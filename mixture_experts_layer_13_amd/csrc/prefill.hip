@@ -527,14 +527,7 @@ bool pf_applies(const GemmArgs& a, bool gemm1) {
 // every workgroup a run of tiles), in multiples of the 8 XCDs; 0 = too few
 // tiles for a persistent launch.
 static int pf_persistent_grid(long long tiles) {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      n = 256;
-    cus = n;
-  }
+  const int cus = device_cu_count();
   long long g = tiles / 4 < cus ? tiles / 4 : cus;
   return (int)(g / 8 * 8);
 }
@@ -551,13 +544,12 @@ template <int T, bool G1>
 static int pf_launch(const GemmArgs& a, hipStream_t st) {
   constexpr int WR = pf_wr<T, G1>();
   using L = PfL<WR>;
-  static bool attr_set = false;  // per process: one device's attribute covers the kernel
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&pf_gemm_kernel<T, G1, WR>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kPfLdsBytes);
-    if (err != hipSuccess) return (int)err;
-    attr_set = true;
-  }
+  static OncePerDevice attr;
+  const int err = attr.run([] {
+    return (int)hipFuncSetAttribute(reinterpret_cast<const void*>(&pf_gemm_kernel<T, G1, WR>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, kPfLdsBytes);
+  });
+  if (err) return err;
   const int ntiles = G1 ? a.N / 128 : a.K / kPfRows;
   const long long rowb = (long long)(G1 ? a.K : a.N) * Family<T>::kBytes;
   const int nchunks = (int)(rowb / kPfChunk);

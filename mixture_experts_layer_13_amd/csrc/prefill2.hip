@@ -653,25 +653,13 @@ bool pfq_applies(const GemmArgs& a, bool gemm1) {
   return gemm1 ? (a.N % 128 == 0) : (a.K % kQRows == 0);
 }
 
-static int pfq_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      n = 256;
-    cus = n;
-  }
-  return cus;
-}
-
 template <int T, bool G1>
 static int pfq_launch(const GemmArgs& a, hipStream_t st) {
   constexpr int NW = pfq_waves<T, G1>();
   const int ntiles = G1 ? a.N / 128 : a.K / kQRows;
   const long long blocks = (long long)a.max_blocks * 128 / kQTok;  // max_blocks counts 128-row blocks
   const long long tasks = (long long)ntiles * blocks;
-  long long g = tasks < pfq_cus() ? tasks : pfq_cus();
+  long long g = tasks < device_cu_count() ? tasks : device_cu_count();
   g = g / 8 * 8;
   if (g < 8) g = 8;
   hipLaunchKernelGGL((pfq_gemm_kernel<T, G1, NW>), dim3((unsigned)g), dim3(NW * 64), 0, st, a, ntiles);

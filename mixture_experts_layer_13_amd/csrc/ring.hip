@@ -563,13 +563,14 @@ struct RingGemm {
   static bool fits(const GemmArgs& a) { return lds(a) <= (size_t)160 * 1024 / WPC; }
   static int launch(const GemmArgs& a, hipStream_t st) {
     const size_t bytes = lds(a);
-    static size_t attr = 0;  // largest dynamic LDS size enabled so far
-    if (bytes > attr) {
-      int err = (int)hipFuncSetAttribute((const void*)ring_gemm_kernel<WT, NCB, D, WPC, G1>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-      if (err) return err;
-      attr = bytes;
-    }
+    // the limit is set once per device to the most any launch may ask (fits())
+    static OncePerDevice attr;
+    const int err = attr.run([] {
+      return (int)hipFuncSetAttribute((const void*)ring_gemm_kernel<WT, NCB, D, WPC, G1>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      160 * 1024 / WPC);
+    });
+    if (err) return err;
     hipLaunchKernelGGL((ring_gemm_kernel<WT, NCB, D, WPC, G1>), dim3(WPC * device_cu_count()),
                        dim3(kRingThreads), bytes, st, a, table_rows(a));
     return (int)hipGetLastError();

@@ -19,9 +19,10 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_align_capacity", "moe_workspace_size",
            "moe_route_topk", "moe_align_permute", "moe_fused_forward", "moe_quantize_act",
-           "moe_set_profile_events", "moe_route_align", "moe_route_project_topk",
+           "moe_fused_forward_profiled", "moe_route_align", "moe_route_project_topk",
            "moe_route_project_workspace_size")
 MOE_QUANT_WORKSPACE_BYTES = 8192
+MOE_WORKSPACE_SCALES_OFFSET = 4096
 
 
 class MoEError(RuntimeError):
@@ -62,8 +63,9 @@ def lib():
         L.moe_fused_forward.restype = ctypes.c_int
         L.moe_quantize_act.argtypes = [vp, i32, i64, vp, vp, vp, vp, sz, vp]
         L.moe_quantize_act.restype = ctypes.c_int
-        L.moe_set_profile_events.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        L.moe_set_profile_events.restype = None
+        L.moe_fused_forward_profiled.argtypes = ([ctypes.POINTER(moe_problem)] + [vp] * 15 +
+                                                 [sz, vp, ctypes.POINTER(ctypes.c_void_p)])
+        L.moe_fused_forward_profiled.restype = ctypes.c_int
         L.moe_route_align.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                       vp, sz, vp]
         L.moe_route_align.restype = ctypes.c_int
@@ -174,12 +176,6 @@ def moe_quantize_act(x, static_scale=None, codes=None, scale=None, workspace=Non
     return codes, scale
 
 
-def moe_set_profile_events(events):
-    """events: four hipEvent_t handles (ints) or None entries."""
-    arr = (ctypes.c_void_p * 4)(*[(e or None) for e in events])
-    lib().moe_set_profile_events(arr)
-
-
 @dataclass
 class Alignment:
     sorted_pair_ids: torch.Tensor
@@ -230,13 +226,20 @@ def moe_route_align(logits, topk, renormalize, block_m, workspace, topk_ids=None
 
 def moe_fused_forward(problem, x, w13, w2, topk_weights, alignment, out, workspace,
                       w13_scale=None, w2_scale=None, a1_scale=None, a2_scale=None,
-                      stream=None):
-    _check(lib().moe_fused_forward(
-        ctypes.byref(problem), _ptr(x), _ptr(w13), _ptr(w2), _ptr(w13_scale), _ptr(w2_scale),
-        _ptr(a1_scale), _ptr(a2_scale), _ptr(topk_weights), _ptr(alignment.sorted_pair_ids),
-        _ptr(alignment.block_expert_ids), _ptr(alignment.expert_offsets),
-        _ptr(alignment.pair_pos), _ptr(alignment.num_padded), _ptr(out), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+                      stream=None, events=None):
+    """events: None, or four hipEvent_t handles (ints or None) recorded around
+    the two GEMM launches (moe_fused_forward_profiled)."""
+    args = (ctypes.byref(problem), _ptr(x), _ptr(w13), _ptr(w2), _ptr(w13_scale),
+            _ptr(w2_scale), _ptr(a1_scale), _ptr(a2_scale), _ptr(topk_weights),
+            _ptr(alignment.sorted_pair_ids), _ptr(alignment.block_expert_ids),
+            _ptr(alignment.expert_offsets), _ptr(alignment.pair_pos),
+            _ptr(alignment.num_padded), _ptr(out), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    if events is None:
+        _check(lib().moe_fused_forward(*args))
+    else:
+        ev = (ctypes.c_void_p * 4)(*[(e or None) for e in events])
+        _check(lib().moe_fused_forward_profiled(*args, ev))
     return out
 
 
@@ -266,10 +269,16 @@ class FusedMoE:
         self.alignment = alloc_alignment(M, topk, E, block_m, device)
         self.out = torch.empty(M, K, dtype=out_dtype, device=device)
 
-    def __call__(self, x, logits, stream=None):
+    def act_scales(self):
+        """Device view of the (s_x, s_h) fp32 pair that the last E4M3 forward
+        left in the workspace (include/moe.h, MOE_WORKSPACE_SCALES_OFFSET)."""
+        o = MOE_WORKSPACE_SCALES_OFFSET
+        return self.workspace[o:o + 8].view(torch.float32)
+
+    def __call__(self, x, logits, stream=None, events=None):
         moe_route_align(logits, self.topk, self.renormalize, self.block_m, self.workspace,
                         self.topk_ids, self.topk_weights, self.alignment, stream)
         moe_fused_forward(self.problem, x, self.w13, self.w2, self.topk_weights, self.alignment,
                           self.out, self.workspace, self.w13_scale, self.w2_scale,
-                          self.a1_scale, self.a2_scale, stream)
+                          self.a1_scale, self.a2_scale, stream, events)
         return self.out

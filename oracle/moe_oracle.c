@@ -110,11 +110,25 @@ uint8_t oracle_e4m3_from_f32(float f) {
   return sign | (uint8_t)best;
 }
 
+/* Values of all 256 E4M3 codes, filled once from oracle_e4m3_to_f64 (a
+ * lookup of the same numbers, so that the expert loops need not re-derive
+ * each weight's value). */
+static double g_e4m3_val[256];
+static int g_e4m3_val_ready = 0;
+
+static void fill_tables(void) {
+  if (!g_e4m3_val_ready) {
+    for (int c = 0; c < 256; ++c) g_e4m3_val[c] = oracle_e4m3_to_f64((uint8_t)c);
+    g_e4m3_val_ready = 1;
+  }
+  (void)oracle_e4m3_from_f32(0.0f); /* the encoder's table */
+}
+
 static double load_elem(int dtype, const void* p, int64_t i) {
   switch (dtype) {
     case ORC_F32: return (double)((const float*)p)[i];
     case ORC_BF16: return oracle_bf16_to_f64(((const uint16_t*)p)[i]);
-    default: return oracle_e4m3_to_f64(((const uint8_t*)p)[i]);
+    default: return g_e4m3_val[((const uint8_t*)p)[i]];
   }
 }
 
@@ -191,6 +205,7 @@ static int cand64_cmp(const void* pa, const void* pb) {
 int oracle_route_project(int x_dtype, const void* x, int w_dtype, const void* wr, int64_t T,
                          int32_t K, int32_t E, int32_t k, int32_t renormalize, double* logits,
                          int32_t* ids, double* w) {
+  fill_tables();
   if (T < 0 || K < 1 || E < 1 || k < 1 || k > E) return 1;
   if ((x_dtype != ORC_F32 && x_dtype != ORC_BF16) || (w_dtype != ORC_F32 && w_dtype != ORC_BF16))
     return 3;
@@ -272,6 +287,7 @@ int oracle_align(const int32_t* ids, int64_t T, int32_t k, int32_t E,
  * per-tensor FP8 scaling is the scheme of [post], "Backend routing for FP8
  * tensor quantization"; 448 is the largest finite E4M3FN magnitude. */
 float oracle_act_scale(int dtype, const void* x, int64_t n) {
+  fill_tables();
   double amax = 0.0;
   for (int64_t i = 0; i < n; ++i) {
     double v = fabs(load_elem(dtype, x, i));
@@ -284,6 +300,7 @@ float oracle_act_scale(int dtype, const void* x, int64_t n) {
 /* code = E4M3(fl32(x / s)), the division done in IEEE binary32. */
 void oracle_quantize_e4m3(int dtype, const void* x, int64_t n, float s,
                           uint8_t* q) {
+  fill_tables();
   for (int64_t i = 0; i < n; ++i) {
     float v = (float)load_elem(dtype, x, i);
     q[i] = oracle_e4m3_from_f32(v / s);
@@ -344,6 +361,7 @@ int oracle_moe_forward(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                        const int32_t* ids, const double* w,
                        const int64_t* tokens, int64_t n_tokens, double* out,
                        float* scales_out) {
+  fill_tables();
   if (T < 0 || H < 1 || I < 1 || E < 1 || k < 1) return 1;
   if (w_dtype == ORC_E4M3 && (!w13_scale || !w2_scale)) return 1;
   int64_t P = T * (int64_t)k;
@@ -357,7 +375,6 @@ int oracle_moe_forward(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
     /* the scale spans all of x; rows are quantised where they are used */
     sx = a1_scale ? *a1_scale : oracle_act_scale(x_dtype, x, T * (int64_t)H);
     int need_all = !a2_scale || !tokens;
-    (void)oracle_e4m3_from_f32(0.0f); /* fill the code table before threads */
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
       int used = need_all;

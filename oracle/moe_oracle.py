@@ -1,8 +1,11 @@
 """ctypes binding of oracle/libmoe_oracle.so (fp64 CPU oracle; test infrastructure).
 
-Every function takes and returns numpy arrays.  Dtype codes: 0 = f32,
-1 = bf16 (raw uint16 bits), 2 = E4M3FN (raw uint8 codes).  The arithmetic
-lives in moe_oracle.c; this file only marshals arguments.
+Only tests/, the smoke check and the CPU-baseline leg of the benchmark use
+this module.  Every function takes and returns numpy arrays.  Dtype codes:
+0 = f32, 1 = bf16 (raw uint16 bits), 2 = E4M3FN (raw uint8 codes).  The
+arithmetic lives in moe_oracle.c; this file marshals arguments, except
+h_scale(), which forms the all-pairs h scale with fp64 library matrix
+products so that it stays affordable at full batch sizes.
 """
 import ctypes
 import os
@@ -180,3 +183,39 @@ def moe_forward(x, w13, w2, ids, weights, w13_scale=None, w2_scale=None,
     if rc:
         raise ValueError(f"oracle_moe_forward failed ({rc})")
     return out[:n], (float(scales[0]), float(scales[1]))
+
+
+def h_scale(x, w13, ids, w13_scale, a1_scale=None):
+    """Dynamic per-tensor scale of the FP8 intermediate over every real pair
+    of the batch (the per-tensor scaling of the AWS post, "Backend routing for
+    FP8 tensor quantization", read as for x): s_h = fl32(amax|h| / 448), with
+    h = SiLU(g) * u, g and u the gate and up projections of the dequantised
+    activations x^ = s_x * E4M3(fl32(x / s_x)) by s13[e] * w13[e].
+
+    Same definition as the dynamic path of moe_forward; here each expert's
+    gate/up product over all of its tokens is one fp64 library matmul
+    (numpy), which only changes the order of the fp64 sums.  x: [T,H] f32 or
+    bf16 bits; w13: [E,2I,H] E4M3 codes; ids: [T,k] (ids index w13's first
+    axis); w13_scale: [E] f32.  Returns (s_x, s_h) as Python floats."""
+    x = np.ascontiguousarray(x)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, H = x.shape
+    E, I2, H2 = w13.shape
+    assert H2 == H and w13.dtype == np.uint8
+    I = I2 // 2
+    k = ids.shape[1]
+    sx = np.float32(a1_scale) if a1_scale is not None else np.float32(act_scale(x))
+    table = np.array([e4m3_to_f64(c) for c in range(256)], np.float64)
+    xh = table[quantize_e4m3(x, float(sx))] * np.float64(sx)
+    flat = ids.reshape(-1)
+    amax = 0.0
+    for e in np.unique(flat):
+        rows = np.nonzero(flat == e)[0] // k  # a token lists an expert at most once
+        W = table[w13[e]] * np.float64(np.float32(w13_scale[e]))
+        xe = xh[rows]
+        g = xe @ W[:I].T
+        u = xe @ W[I:].T
+        h = g / (1.0 + np.exp(-g)) * u
+        amax = max(amax, float(np.abs(h).max()))
+    sh = np.float32(amax / 448.0) if amax > 0 else np.float32(1.0)
+    return float(sx), float(sh)

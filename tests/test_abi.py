@@ -183,5 +183,52 @@ def test_quantize_rejects_without_launch():
     assert L.moe_quantize_act(f, moe.MOE_BF16, 0, None, f, f, f, 8192, None) == moe.MOE_OK
 
 
-def test_profile_hook_is_host_only():
-    moe.moe_set_profile_events([None, None, None, None])
+def test_profiled_forward_validates_like_the_plain_call():
+    p = _prob()
+    ev = (ctypes.c_void_p * 4)(None, None, None, None)
+    L = moe.lib()
+
+    def fwd(prob, **kw):
+        a = dict(a=FAKE, w13=FAKE, ws=FAKE, wsb=1 << 40)
+        a.update(kw)
+        return L.moe_fused_forward_profiled(ctypes.byref(prob), a["a"], a["w13"], FAKE, None, None,
+                                            None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            ctypes.c_void_p(0x7f0100000000), a["ws"], a["wsb"],
+                                            None, ev)
+    assert fwd(_prob(K=96)) == moe.MOE_ERR_SHAPE
+    assert fwd(p, w13=None) == moe.MOE_ERR_NULL
+    assert fwd(p, wsb=16) == moe.MOE_ERR_WORKSPACE
+    assert fwd(_prob(M=0)) == moe.MOE_OK
+
+
+def test_host_calls_from_many_threads():
+    """Validation, sizing and error reporting from 8 threads at once: every
+    thread sees the single-threaded results and its own last error (the
+    library keeps no shared mutable state on these paths)."""
+    import threading
+
+    probs = [_prob(M=m, block_m=bm, w_dtype=wd) for m in (1, 64, 4096, 8192)
+             for bm in (16, 128, 256) for wd in (moe.MOE_BF16, moe.MOE_FP8_E4M3)]
+    want = [_ws(p) for p in probs]
+    L = moe.lib()
+    errors = []
+
+    def worker(tid):
+        try:
+            for it in range(300):
+                i = (tid * 7 + it) % len(probs)
+                assert _ws(probs[i]) == want[i]
+                bad = _prob(K=96 + 128 * tid)
+                assert _fwd(bad) == moe.MOE_ERR_SHAPE
+                msg = L.moe_last_error().decode()
+                assert f"K={96 + 128 * tid} " in msg, msg
+                assert L.moe_align_capacity(it, 8, 64, 16) == it * 8 + min(64, it * 8) * 15
+        except AssertionError as e:  # pragma: no cover - reported below
+            errors.append((tid, e))
+
+    th = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not errors, errors[:3]

@@ -9,7 +9,10 @@ cost, a kernel family's code-object loading included).  A warm pass checks,
 per M, that the route -> align -> forward calls do not lower the device's
 free memory (the library allocates nothing) and that they capture into
 a HIP graph (capture fails on any synchronisation) whose replays equal the
-eager result bit for bit.
+eager result bit for bit; the eager result of every M is checked against
+the fp64 oracle (every token up to M = 16, else the token of the last real
+pair of every expert segment plus a seeded fill; E4M3 with the dynamic h
+scale against the oracle's all-pairs scale).
 """
 import time
 
@@ -17,6 +20,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from mixture_experts_layer_13_amd import inputs, moe
 from tests import harness as H
 
@@ -105,6 +109,19 @@ def test_launch_path_sweep(wl):
         # runtime releases an earlier size's graph in the meantime
         assert free1 >= free0, (M, free0, free1)
         eager = views(M)[4].clone()
+        # the eager result against the oracle
+        dm = dict(d, x=x[:M], logits=logits[:M], T=M)
+        rids, _ = oracle.route_topk(logits[:M].cpu().numpy(), k, True)
+        assert np.array_equal(views(M)[2].cpu().numpy(), rids), M
+        tokens = H.sample_tokens(rids, 16, seed=M)
+        if w.fp8_act:
+            o = moe.MOE_WORKSPACE_SCALES_OFFSET
+            H.check_fp8_dynamic(dm, ws[o:o + 8].view(torch.float32), eager, tokens, f"M={M}")
+        else:
+            ref, _, _, _ = H.oracle_forward(dm, tokens=tokens)
+            err = H.row_rel_err(H.to_f64(eager)[tokens], ref)
+            H.say(f"  M={M}: {len(tokens)} rows, max row rel err {err:.3e}")
+            assert err <= H.BF16_TOL, (M, err)
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())

@@ -367,6 +367,21 @@ def test_forward_fp8_matches_torch_cast_bruteforce():
     np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-13)
 
 
+@pytest.mark.parametrize("seed,T,H,I,E,k", [(21, 9, 64, 32, 6, 3), (31, 40, 256, 128, 8, 2),
+                                           (41, 17, 128, 64, 16, 4)])
+def test_h_scale_matches_the_forward_dynamic_scale(seed, T, H, I, E, k):
+    """The all-pairs h scale by fp64 library matmuls equals the scale the
+    forward's own per-pair loops pick (same definition, other sum order)."""
+    d = _fp8_case(T=T, H=H, I=I, E=E, k=k, seed=seed)
+    ids, w = oracle.route_topk(d["logits"], d["topk"], True)
+    _, (sx, sh) = oracle.moe_forward(d["x"], d["w13"], d["w2"], ids, w, d["w13_scale"],
+                                     d["w2_scale"], fp8_act=True)
+    assert oracle.h_scale(d["x"], d["w13"], ids, d["w13_scale"]) == (sx, sh)
+    _, (_, sh2) = oracle.moe_forward(d["x"], d["w13"], d["w2"], ids, w, d["w13_scale"],
+                                     d["w2_scale"], fp8_act=True, a1_scale=0.03)
+    assert oracle.h_scale(d["x"], d["w13"], ids, d["w13_scale"], a1_scale=0.03) == (np.float32(0.03), sh2)
+
+
 def test_forward_fp8_weights_without_act_quant_match_dense_gated():
     d = _fp8_case(seed=22)
     ids, w = oracle.route_topk(d["logits"], d["topk"], True)
