@@ -116,6 +116,85 @@ def oracle_h_scale(d, ids):
     return oracle.h_scale(inputs.to_numpy_bits(d["x"]), w13, remap[ids], s13)
 
 
+# Bound on the GPU's error in an E4M3 gate or up sum, relative to the sum of
+# the magnitudes of its terms.  Measured on the 128-row E4M3 gate/up kernel
+# (500-element sums): at most 6.2e-6 = 2^-17.3 of sum|t|, more than fp32
+# accumulation alone would give, so the E4M3 MFMA's own accumulation is
+# coarser than fp32; 2^-16 is the bound taken.
+GATE_UP_EPS = 2.0 ** -16
+
+# E4M3FN magnitudes of the 127 non-negative finite codes, ascending.
+_E4M3_MAG = None
+
+
+def _e4m3_mags():
+    global _E4M3_MAG
+    if _E4M3_MAG is None:
+        _E4M3_MAG = np.array([oracle.e4m3_to_f64(c) for c in range(0x7F)], np.float64)
+    return _E4M3_MAG
+
+
+def flip_allowance(d, tokens, s_h, delta_s=0.0):
+    """Per sampled token, the most its output row can move because E4M3 codes
+    of h are decided on the far side of a rounding midpoint.  Encoding is a
+    step function: where h / s_h lies within the GPU's error of the midpoint
+    between two codes, either code is a correct rounding of a value that is
+    itself correct within that error.  For each h element of the token's
+    pairs (fp64, from the oracle's dequantised operands) the window is
+    GATE_UP_EPS * (|dh/dg| S_g + |dh/du| S_u) + 2^-22 |h| (SiLU and scale
+    roundings), plus delta_s * |h| for a scale that differs by delta_s; an
+    element whose window holds a midpoint may take either neighbouring code,
+    which moves out[t, n] by at most w_j * |w2[e, n, i]| * gap * s_h.
+    Returns the absolute allowances [len(tokens), H]."""
+    mags = _e4m3_mags()
+    mids = (mags[1:] + mags[:-1]) / 2.0
+    ids, wts = oracle.route_topk(d["logits"].cpu().numpy(), d["topk"], True)
+    ids_t = ids[tokens]
+    experts = np.unique(ids_t)
+    sel = torch.as_tensor(experts, device=d["w13"].device, dtype=torch.long)
+    table = np.array([oracle.e4m3_to_f64(c) for c in range(256)], np.float64)
+    s13 = d["w13_scale"].index_select(0, sel).cpu().numpy().astype(np.float64)
+    s2 = d["w2_scale"].index_select(0, sel).cpu().numpy().astype(np.float64)
+    w13 = inputs.to_numpy_bits(d["w13"].index_select(0, sel))
+    w2 = inputs.to_numpy_bits(d["w2"].index_select(0, sel))
+    xb = inputs.to_numpy_bits(d["x"])
+    sx = np.float32(oracle.act_scale(xb))
+    xh = table[oracle.quantize_e4m3(xb[tokens], float(sx))] * np.float64(sx)
+    I = w13.shape[1] // 2
+    allow = np.zeros((len(tokens), w2.shape[1]))
+    for c, e in enumerate(experts):
+        rows, slots = np.nonzero(ids_t == e)
+        W = table[w13[c]] * s13[c]
+        g = xh[rows] @ W[:I].T
+        u = xh[rows] @ W[I:].T
+        Sg = np.abs(xh[rows]) @ np.abs(W[:I]).T
+        Su = np.abs(xh[rows]) @ np.abs(W[I:]).T
+        sg = 1.0 / (1.0 + np.exp(-g))
+        h = g * sg * u
+        dh_dg = np.abs(sg * (1.0 + g * (1.0 - sg)) * u)
+        win = (GATE_UP_EPS * (dh_dg * Sg + np.abs(g * sg) * Su) + (2.0 ** -22 + delta_s) * np.abs(h)) / s_h
+        q = np.minimum(np.abs(h) / s_h, 448.0)
+        m = np.searchsorted(mids, q)  # nearest midpoints: mids[m - 1] <= q < mids[m]
+        lo = np.clip(m - 1, 0, len(mids) - 1)
+        hi = np.clip(m, 0, len(mids) - 1)
+        near_lo = np.abs(q - mids[lo]) <= win
+        near_hi = np.abs(q - mids[hi]) <= win
+        gap = np.where(near_hi, mags[np.minimum(hi + 1, len(mags) - 1)] - mags[hi],
+                       np.where(near_lo, mags[lo + 1] - mags[lo], 0.0))
+        W2a = np.abs(table[w2[c]]) * s2[c]  # [H, I]
+        a = (gap * s_h * wts[tokens[rows], slots][:, None]) @ W2a.T  # [rows, H]
+        np.add.at(allow, rows, a)
+    return allow
+
+
+def row_err_with_allowance(got, ref, allow, tol):
+    """max over rows of max_n (|g - r| - allow)+ / max|r|, to compare with tol."""
+    num = np.maximum(np.abs(np.asarray(got, np.float64) - ref) - allow, 0.0).max(axis=1)
+    den = np.abs(ref).max(axis=1)
+    den = np.where(den == 0, 1.0, den)
+    return float((num / den).max()) if len(num) else 0.0
+
+
 def check_fp8_dynamic(d, scales, out, tokens, label, tol_own=FP8_TOL):
     """FP8 with the dynamic h scale.  (1) s_x bit-exact and s_h within
     SH_REL_TOL of the oracle's all-pairs scales; (2) the sampled rows against
@@ -137,6 +216,14 @@ def check_fp8_dynamic(d, scales, out, tokens, label, tol_own=FP8_TOL):
     say(f"  {label}: s_h gpu {s_gpu[1]:.9g} oracle {sh_o:.9g} (rel {rel:.2e}); "
         f"rows {len(tokens)}: err at gpu s_h {err_g:.3e}, at oracle s_h {err_o:.3e}")
     assert rel <= SH_REL_TOL, rel
-    assert err_g <= FP8_TOL, err_g
-    assert err_o <= tol_own, err_o
+    if err_g > FP8_TOL or err_o > tol_own:
+        # rows past the bar must be explained by codes decided at a midpoint
+        ag = flip_allowance(d, tokens, float(s_gpu[1]))
+        ao = flip_allowance(d, tokens, sh_o, delta_s=rel)
+        eg = row_err_with_allowance(got, ref_g, ag, FP8_TOL)
+        eo = row_err_with_allowance(got, ref_o, ao, tol_own)
+        say(f"    beyond the codes decided within the GPU's error of a midpoint: "
+            f"{eg:.3e} at gpu s_h, {eo:.3e} at oracle s_h")
+        assert eg <= FP8_TOL, eg
+        assert eo <= tol_own, eo
     return rel, err_g, err_o
