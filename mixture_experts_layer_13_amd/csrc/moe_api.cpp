@@ -82,8 +82,9 @@ Layout layout_of(const moe_problem& p) {
   o = up256(o + (size_t)cap * p.N * (fp8 ? 4 : 2));
   L.hq = o;
   if (fp8) o = up256(o + (size_t)cap * p.N);
-  L.y = o;  // per-pair down-projection rows (every path but the f32-weight decode kernel)
-  o = up256(o + (size_t)cap * p.K * 4);
+  L.y = o;  // per-pair down-projection rows in the output dtype (every path but the
+            // f32-weight decode kernel)
+  o = up256(o + (size_t)cap * p.K * dtype_bytes(p.out_dtype));
   L.total = o;
   return L;
 }
