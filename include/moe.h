@@ -268,6 +268,31 @@ moe_status moe_quantize_act(const void* x, int32_t x_dtype, int64_t n,
                             size_t workspace_bytes, void* stream);
 
 /*
+ * moe_fused_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments and errors, without the
+ * workspace arguments.  The workspace is a device array inside the library,
+ * MOE_NOALLOC_SCRATCH_BYTES per device, held from the first call on a device
+ * until the process ends; the call itself allocates nothing.  Problems whose
+ * moe_workspace_size exceeds it are rejected with MOE_ERR_WORKSPACE (the
+ * decode shapes of H = 4096, I = 1024, E = 64, top-8 up to M = 64, bf16 or
+ * E4M3 weights, need about 20 MiB).  Every call on a device uses that
+ * device's one array: calls that overlap in time on one device (several
+ * streams or threads) race and must be serialised by the caller.  The array
+ * needs no initialisation; after an E4M3 call it holds s_x and s_h at
+ * MOE_WORKSPACE_SCALES_OFFSET like a caller workspace.  The device is the
+ * current one; `stream` must belong to it.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_fused_forward_noalloc(
+    const moe_problem* p, const void* a, const void* w13, const void* w2,
+    const float* w13_scale, const float* w2_scale, const float* a1_scale,
+    const float* a2_scale, const float* topk_weights,
+    const int32_t* sorted_pair_ids, const int32_t* block_expert_ids,
+    const int32_t* expert_offsets, const int32_t* pair_pos,
+    const int32_t* num_padded, void* out, void* stream);
+
+/*
  * moe_fused_forward with timing events: the same computation, arguments and
  * errors, and in addition hipEventRecord of events[0] / events[1] (hipEvent_t
  * passed as void*) on `stream` right before and after the gate/up GEMM

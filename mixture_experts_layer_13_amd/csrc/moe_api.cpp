@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "launch.hpp"
@@ -399,6 +400,32 @@ moe_status fused_forward(const moe_problem* p, const void* a, const void* w13, c
   return ok();
 }
 
+// Workspace of moe_fused_forward_noalloc: one array per device, kept for the
+// life of the process.  Its name is a host-side stand-in for the device
+// address; host code uses only the address that hipGetSymbolAddress returns
+// for the current device.
+constexpr size_t kScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::once_flag g_scratch_once[moe::kMaxDevices];
+void* g_scratch_ptr[moe::kMaxDevices];
+int g_scratch_err[moe::kMaxDevices];
+
+// Device address of this device's scratch array (looked up once per device,
+// with that device current); 0 or a hipError_t.
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= moe::kMaxDevices)
+    return (int)hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = (int)hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = ptr;
+  });
+  *out = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -413,6 +440,31 @@ moe_status moe_fused_forward(const moe_problem* p, const void* a, const void* w1
   return fused_forward(p, a, w13, w2, w13_scale, w2_scale, a1_scale, a2_scale, topk_weights,
                        sorted_pair_ids, block_expert_ids, expert_offsets, pair_pos, num_padded,
                        out, workspace, workspace_bytes, stream, nullptr);
+}
+
+moe_status moe_fused_forward_noalloc(
+    const moe_problem* p, const void* a, const void* w13, const void* w2,
+    const float* w13_scale, const float* w2_scale, const float* a1_scale, const float* a2_scale,
+    const float* topk_weights, const int32_t* sorted_pair_ids, const int32_t* block_expert_ids,
+    const int32_t* expert_offsets, const int32_t* pair_pos, const int32_t* num_padded, void* out,
+    void* stream) {
+  moe_status s = check_problem(p);
+  if (s) return s;
+  size_t need = 0;
+  s = moe_workspace_size(p, &need);
+  if (s) return s;
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "problem needs %zu bytes of workspace; moe_fused_forward_noalloc holds at most %zu "
+                "(use moe_fused_forward with a caller workspace)",
+                need, kScratchBytes);
+  if (p->M == 0) return ok();
+  void* ws = nullptr;
+  int err = scratch_address(&ws);
+  if (err) return hip_status(err, "scratch address lookup");
+  return fused_forward(p, a, w13, w2, w13_scale, w2_scale, a1_scale, a2_scale, topk_weights,
+                       sorted_pair_ids, block_expert_ids, expert_offsets, pair_pos, num_padded,
+                       out, ws, kScratchBytes, stream, nullptr);
 }
 
 moe_status moe_fused_forward_profiled(

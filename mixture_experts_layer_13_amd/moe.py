@@ -19,10 +19,11 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_align_capacity", "moe_workspace_size",
            "moe_route_topk", "moe_align_permute", "moe_fused_forward", "moe_quantize_act",
-           "moe_fused_forward_profiled", "moe_route_align", "moe_route_project_topk",
+           "moe_fused_forward_profiled", "moe_fused_forward_noalloc", "moe_route_align", "moe_route_project_topk",
            "moe_route_project_workspace_size")
 MOE_QUANT_WORKSPACE_BYTES = 8192
 MOE_WORKSPACE_SCALES_OFFSET = 4096
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoEError(RuntimeError):
@@ -66,6 +67,8 @@ def lib():
         L.moe_fused_forward_profiled.argtypes = ([ctypes.POINTER(moe_problem)] + [vp] * 15 +
                                                  [sz, vp, ctypes.POINTER(ctypes.c_void_p)])
         L.moe_fused_forward_profiled.restype = ctypes.c_int
+        L.moe_fused_forward_noalloc.argtypes = [ctypes.POINTER(moe_problem)] + [vp] * 15
+        L.moe_fused_forward_noalloc.restype = ctypes.c_int
         L.moe_route_align.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                       vp, sz, vp]
         L.moe_route_align.restype = ctypes.c_int
@@ -174,6 +177,19 @@ def moe_quantize_act(x, static_scale=None, codes=None, scale=None, workspace=Non
                                   workspace.numel() * workspace.element_size(),
                                   _stream(stream)))
     return codes, scale
+
+
+def moe_fused_forward_noalloc(problem, x, w13, w2, topk_weights, alignment, out,
+                              w13_scale=None, w2_scale=None, a1_scale=None, a2_scale=None,
+                              stream=None):
+    """moe_fused_forward on the library's own per-device scratch array (no
+    workspace argument; nothing is allocated by the call)."""
+    _check(lib().moe_fused_forward_noalloc(
+        ctypes.byref(problem), _ptr(x), _ptr(w13), _ptr(w2), _ptr(w13_scale), _ptr(w2_scale),
+        _ptr(a1_scale), _ptr(a2_scale), _ptr(topk_weights), _ptr(alignment.sorted_pair_ids),
+        _ptr(alignment.block_expert_ids), _ptr(alignment.expert_offsets),
+        _ptr(alignment.pair_pos), _ptr(alignment.num_padded), _ptr(out), _stream(stream)))
+    return out
 
 
 @dataclass

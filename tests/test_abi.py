@@ -232,3 +232,35 @@ def test_host_calls_from_many_threads():
     for t in th:
         t.join()
     assert not errors, errors[:3]
+
+
+class _Fake:
+    """Stands in for a device tensor: a fixed, never dereferenced address."""
+
+    def __init__(self, addr=0x7f0000001000):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+class _FakeStream:
+    cuda_stream = 0
+
+
+def test_noalloc_forward_rejects_oversized_problem_without_launch():
+    # a prefill-sized problem needs far more workspace than the scratch array
+    p = moe.make_problem(8192, 4096, 1024, 64, 8, 256, moe.torch.bfloat16, moe.torch.bfloat16,
+                         moe.torch.bfloat16)
+    assert moe.moe_workspace_size(p) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    f = _Fake()
+    al = moe.Alignment(f, f, f, f, f, 256)
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_fused_forward_noalloc(p, f, f, f, f, al, _Fake(0x7f0100000000), stream=_FakeStream())
+    assert e.value.status == moe.MOE_ERR_WORKSPACE and "noalloc" in str(e.value)
+    # invalid shapes and NULL pointers as for the workspace call
+    q = moe.make_problem(64, 96, 1024, 64, 8, 16, moe.torch.bfloat16, moe.torch.bfloat16,
+                         moe.torch.bfloat16)
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_fused_forward_noalloc(q, f, f, f, f, al, _Fake(0x7f0100000000), stream=_FakeStream())
+    assert e.value.status == moe.MOE_ERR_SHAPE
