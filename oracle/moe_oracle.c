@@ -39,6 +39,11 @@
  *     encoding rounds to nearest, ties to even, saturating at +-448;
  *   - activation scale s = fl32(amax / 448) (1 when amax = 0); the code of x
  *     is E4M3(fl32(x / s)) with an IEEE fp32 division;
+ *   - rotary position embedding with per-head E4M3 quantisation
+ *     (oracle_rope_quant_per_head): the inverse-frequency table is an input,
+ *     the angle of pair i of token t is fl32(pos[t] * inv_freq[i]), the pair
+ *     is rotated by that angle (by its negative when `inverse`), pairs are
+ *     (i, i + D/2) or (2i, 2i + 1); one scale per head over the call's tokens;
  *   - the intermediate h is quantised with one dynamic scale over all real
  *     pairs, the same per-tensor rule as x: s_h = fl32(amax|h| / 448) with
  *     amax taken over the fp64 values; its code is E4M3(fl32(h / s_h)), the
@@ -455,5 +460,70 @@ int oracle_moe_forward(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
   free(xd);
   free(a);
   free(y);
+  return 0;
+}
+
+/* ------------------------------------------ rotary embedding + per-head FP8 */
+
+/*
+ * Rotary position embedding fused with per-head FP8 quantisation, the kernel
+ * the AWS post names in "Triton JIT recompilation elimination" (rotary
+ * position embedding and FP8 quantisation fused, per head).  The pages give no
+ * formula; the reading taken here:
+ *   x [T, nH, D] (f32 or bf16), D even; positions pos [T]; the inverse
+ *   frequencies inv_freq [D/2] (fp32, an input: the "inv" table of RoPE,
+ *   base^(-2i/D) in the usual construction).
+ *   angle a(t, i) = fl32(pos[t] * inv_freq[i]), negated when `inverse`;
+ *   each pair (u, v) of head h -- u = x[t,h,i], v = x[t,h,i + D/2] (halves),
+ *   or u = x[t,h,2i], v = x[t,h,2i+1] (interleaved) -- becomes
+ *     u' = u cos a - v sin a,   v' = v cos a + u sin a      (fp64);
+ *   per head h: s_h = fl32(amax over t and d of |y[t,h,d]| / 448), 1 when the
+ *   amax is 0, or static_scales[h] when given; codes E4M3(fl32(y / s_h)).
+ * y_out (optional, fp64 [T, nH, D]) receives the rotated values.
+ */
+int oracle_rope_quant_per_head(int32_t x_dtype, const void* x, const int32_t* pos,
+                               const float* inv_freq, int64_t T, int32_t nH, int32_t D,
+                               int32_t interleaved, int32_t inverse, const float* static_scales,
+                               uint8_t* codes, float* scales, double* y_out) {
+  if (T < 0 || nH < 1 || D < 2 || D % 2) return 1;
+  if (x_dtype != ORC_F32 && x_dtype != ORC_BF16) return 3;
+  fill_tables();
+  const int32_t half = D / 2;
+  const int64_t n = T * (int64_t)nH * D;
+  double* y = y_out ? y_out : (double*)malloc(sizeof(double) * (size_t)(n + 1));
+  double* amax = (double*)calloc((size_t)nH, sizeof(double));
+  if (!y || !amax) return 2;
+  for (int64_t t = 0; t < T; ++t) {
+    for (int32_t i = 0; i < half; ++i) {
+      float a32 = (float)((double)pos[t] * (double)inv_freq[i]);
+      double a = inverse ? -(double)a32 : (double)a32;
+      double c = cos(a), sn = sin(a);
+      for (int32_t h = 0; h < nH; ++h) {
+        int64_t base = (t * nH + h) * (int64_t)D;
+        int64_t iu = base + (interleaved ? 2 * i : i);
+        int64_t iv = base + (interleaved ? 2 * i + 1 : i + half);
+        double u = load_elem(x_dtype, x, iu), v = load_elem(x_dtype, x, iv);
+        y[iu] = u * c - v * sn;
+        y[iv] = v * c + u * sn;
+      }
+    }
+  }
+  for (int64_t t = 0; t < T; ++t)
+    for (int32_t h = 0; h < nH; ++h)
+      for (int32_t d = 0; d < D; ++d) {
+        double v = fabs(y[(t * nH + h) * (int64_t)D + d]);
+        if (v > amax[h]) amax[h] = v;
+      }
+  for (int32_t h = 0; h < nH; ++h)
+    scales[h] = static_scales ? static_scales[h]
+                              : (amax[h] == 0.0 ? 1.0f : (float)(amax[h] / 448.0));
+  for (int64_t t = 0; t < T; ++t)
+    for (int32_t h = 0; h < nH; ++h)
+      for (int32_t d = 0; d < D; ++d) {
+        int64_t k = (t * nH + h) * (int64_t)D + d;
+        codes[k] = oracle_e4m3_from_f32((float)(y[k] / (double)scales[h]));
+      }
+  if (!y_out) free(y);
+  free(amax);
   return 0;
 }

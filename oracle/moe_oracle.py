@@ -47,6 +47,9 @@ def lib():
                                          c_i32, vp, c_i32, vp, vp, vp, vp,
                                          c_i32, vp, vp, vp, vp, vp, c_i64, vp, vp]
         L.oracle_moe_forward.restype = ctypes.c_int
+        L.oracle_rope_quant_per_head.argtypes = [c_i32, vp, vp, vp, c_i64, c_i32, c_i32, c_i32,
+                                                 c_i32, vp, vp, vp, vp]
+        L.oracle_rope_quant_per_head.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -219,3 +222,27 @@ def h_scale(x, w13, ids, w13_scale, a1_scale=None):
         amax = max(amax, float(np.abs(h).max()))
     sh = np.float32(amax / 448.0) if amax > 0 else np.float32(1.0)
     return float(sx), float(sh)
+
+
+def rope_quant_per_head(x, positions, inv_freq, interleaved=False, inverse=False,
+                        static_scales=None, want_y=False):
+    """Rotary embedding then per-head E4M3 codes (moe_oracle.c,
+    oracle_rope_quant_per_head).  x: [T, nH, D] float32 or uint16 (bf16
+    bits); positions: [T] int32; inv_freq: [D/2] float32.  Returns (codes
+    uint8 [T, nH, D], scales f32 [nH]) and, with want_y, the fp64 rotated
+    values."""
+    x = np.ascontiguousarray(x)
+    T, nH, D = x.shape
+    pos = np.ascontiguousarray(positions, dtype=np.int32)
+    invf = np.ascontiguousarray(inv_freq, dtype=np.float32)
+    assert pos.shape == (T,) and invf.shape == (D // 2,)
+    codes = np.zeros((T, nH, D), np.uint8)
+    scales = np.zeros(nH, np.float32)
+    y = np.zeros((T, nH, D), np.float64) if want_y else None
+    st = None if static_scales is None else np.ascontiguousarray(static_scales, dtype=np.float32)
+    rc = lib().oracle_rope_quant_per_head(_dtype_code(x), _p(x), _p(pos), _p(invf), T, nH, D,
+                                          int(bool(interleaved)), int(bool(inverse)), _p(st),
+                                          _p(codes), _p(scales), _p(y))
+    if rc:
+        raise ValueError(f"oracle_rope_quant_per_head failed ({rc})")
+    return (codes, scales, y) if want_y else (codes, scales)
