@@ -310,6 +310,46 @@ moe_status moe_fused_forward_profiled(
     const int32_t* num_padded, void* out, void* workspace,
     size_t workspace_bytes, void* stream, void* const events[4]);
 
+/*
+ * Rotary position embedding fused with per-head FP8 quantisation: the kernel
+ * that the AWS post names in "Triton JIT recompilation elimination" (rotary
+ * position embedding and FP8 quantisation fused, per head), whose token count
+ * must never trigger a recompile.  The pages give no formula; this call reads
+ * it as follows, for x [T, n_heads, head_dim] (D = head_dim):
+ *   angle a(t, i) = fl32(positions[t] * inv_freq[i]), i < D/2, negated when
+ *     `inverse` (the rotation back);
+ *   pairs (x[t,h,i], x[t,h,i+D/2]) (interleaved == 0) or
+ *     (x[t,h,2i], x[t,h,2i+1]) (interleaved != 0); (u, v) becomes
+ *     (u cos a - v sin a, v cos a + u sin a), computed in fp32;
+ *   one scale per head over the call's T tokens:
+ *     scales[h] = static_scales ? static_scales[h]
+ *                               : fl32(amax over t, d of |y[t,h,d]| / 448)
+ *     (1 when that amax is 0);
+ *   codes[t,h,d] = E4M3(fl32(y[t,h,d] / scales[h])), round to nearest even,
+ *     saturating at +-448 (OCP E4M3FN).
+ * x          device [T, n_heads, head_dim] of x_dtype (MOE_BF16 or MOE_F32),
+ *            16-byte aligned.
+ * positions  device int32 [T], |positions[t]| < 2^24.
+ * inv_freq   device f32 [head_dim / 2] (e.g. base^(-2i/D)).
+ * static_scales  device f32 [n_heads] or NULL (dynamic).
+ * codes      device uint8 [T, n_heads, head_dim] (written), 16-byte aligned.
+ * scales     device f32 [n_heads] (written: the scales used).
+ * workspace  device, >= moe_rope_workspace_size() bytes, 16-byte aligned (no
+ *            initialisation, not preserved).
+ * Limits: 1 <= n_heads <= 256; head_dim a multiple of 16 in [16, 2048].
+ * T == 0 is a no-op.  Errors: MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_NULL,
+ * MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_HIP; nothing is enqueued on an
+ * error.  T is only ever a kernel argument.
+ */
+moe_status moe_rope_quantize_per_head(const void* x, int32_t x_dtype, const int32_t* positions,
+                                      const float* inv_freq, int32_t T, int32_t n_heads,
+                                      int32_t head_dim, int32_t interleaved, int32_t inverse,
+                                      const float* static_scales, uint8_t* codes, float* scales,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace moe_rope_quantize_per_head needs.  Host only. */
+moe_status moe_rope_workspace_size(int32_t T, int32_t n_heads, int32_t head_dim, size_t* bytes);
+
 #ifdef __cplusplus
 }
 #endif

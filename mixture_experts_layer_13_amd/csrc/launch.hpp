@@ -61,6 +61,13 @@ int launch_quant_h(const float* h32, int N, int max_rows, const int32_t* num_row
                    const uint32_t* hmax_bits, const float* static_scale,
                    uint8_t* hq, float* sh, hipStream_t stream);
 
+// Rotary embedding + per-head E4M3 quantisation (rope.hip); x [T, nH, D]
+// bf16 or f32, D % 16 == 0, nH <= 256; ws holds rope_workspace_bytes().
+size_t rope_workspace_bytes(int T, int nH, int D);
+int launch_rope_quant(const void* x, int xt, const int32_t* pos, const float* inv_freq, int T,
+                      int nH, int D, int interleaved, int inverse, const float* static_scales,
+                      uint8_t* codes, float* scales, void* ws, hipStream_t st);
+
 // Arguments of the expert GEMMs (device pointers unless noted).
 struct GemmArgs {
   int M, K, N, E, topk, block_m, P;  // host values

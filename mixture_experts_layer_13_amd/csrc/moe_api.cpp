@@ -478,6 +478,50 @@ moe_status moe_fused_forward_profiled(
                        out, workspace, workspace_bytes, stream, events);
 }
 
+static moe_status check_rope_dims(int32_t T, int32_t n_heads, int32_t head_dim) {
+  if (T < 0) return fail(MOE_ERR_SHAPE, "T=%d must be >= 0", T);
+  if (n_heads < 1 || n_heads > 256) return fail(MOE_ERR_SHAPE, "n_heads=%d must be in [1, 256]", n_heads);
+  if (head_dim < 16 || head_dim > 2048 || head_dim % 16)
+    return fail(MOE_ERR_SHAPE, "head_dim=%d must be a multiple of 16 in [16, 2048]", head_dim);
+  if ((long long)T * n_heads * head_dim > (1LL << 34))
+    return fail(MOE_ERR_SHAPE, "T*n_heads*head_dim too large");
+  return MOE_OK;
+}
+
+moe_status moe_rope_workspace_size(int32_t T, int32_t n_heads, int32_t head_dim, size_t* bytes) {
+  if (!bytes) return fail(MOE_ERR_NULL, "bytes is NULL");
+  moe_status s = check_rope_dims(T, n_heads, head_dim);
+  if (s) return s;
+  *bytes = moe::rope_workspace_bytes(T, n_heads, head_dim);
+  return ok();
+}
+
+moe_status moe_rope_quantize_per_head(const void* x, int32_t x_dtype, const int32_t* positions,
+                                      const float* inv_freq, int32_t T, int32_t n_heads,
+                                      int32_t head_dim, int32_t interleaved, int32_t inverse,
+                                      const float* static_scales, uint8_t* codes, float* scales,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status s = check_rope_dims(T, n_heads, head_dim);
+  if (s) return s;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16)
+    return fail(MOE_ERR_DTYPE, "x_dtype must be MOE_F32 or MOE_BF16");
+  if (T == 0) return ok();
+  if (!x || !positions || !inv_freq || !codes || !scales || !workspace)
+    return fail(MOE_ERR_NULL, "x, positions, inv_freq, codes, scales and workspace are required");
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(workspace, 16))
+    return fail(MOE_ERR_ALIGN, "x, codes and workspace must be 16-byte aligned");
+  if (!aligned(positions, 4) || !aligned(inv_freq, 4) || !aligned(scales, 4) ||
+      !aligned(static_scales, 4))
+    return fail(MOE_ERR_ALIGN, "positions, inv_freq and scales must be 4-byte aligned");
+  const size_t need = moe::rope_workspace_bytes(T, n_heads, head_dim);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  int err = moe::launch_rope_quant(x, x_dtype, positions, inv_freq, T, n_heads, head_dim,
+                                   interleaved ? 1 : 0, inverse ? 1 : 0, static_scales, codes,
+                                   scales, workspace, (hipStream_t)stream);
+  return hip_status(err, "rope launch");
+}
+
 moe_status moe_quantize_act(const void* x, int32_t x_dtype, int64_t n, const float* static_scale,
                             uint8_t* codes, float* scale, void* workspace,
                             size_t workspace_bytes, void* stream) {

@@ -20,7 +20,7 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_align_capacity", "moe_workspace_size",
            "moe_route_topk", "moe_align_permute", "moe_fused_forward", "moe_quantize_act",
            "moe_fused_forward_profiled", "moe_fused_forward_noalloc", "moe_route_align", "moe_route_project_topk",
-           "moe_route_project_workspace_size")
+           "moe_route_project_workspace_size", "moe_rope_quantize_per_head", "moe_rope_workspace_size")
 MOE_QUANT_WORKSPACE_BYTES = 8192
 MOE_WORKSPACE_SCALES_OFFSET = 4096
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -77,6 +77,11 @@ def lib():
         L.moe_route_project_topk.restype = ctypes.c_int
         L.moe_route_project_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.moe_route_project_workspace_size.restype = ctypes.c_int
+        L.moe_rope_quantize_per_head.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp,
+                                                 vp, vp, sz, vp]
+        L.moe_rope_quantize_per_head.restype = ctypes.c_int
+        L.moe_rope_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+        L.moe_rope_workspace_size.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -190,6 +195,32 @@ def moe_fused_forward_noalloc(problem, x, w13, w2, topk_weights, alignment, out,
         _ptr(alignment.block_expert_ids), _ptr(alignment.expert_offsets),
         _ptr(alignment.pair_pos), _ptr(alignment.num_padded), _ptr(out), _stream(stream)))
     return out
+
+
+def moe_rope_workspace_size(T, n_heads, head_dim):
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_rope_workspace_size(T, n_heads, head_dim, ctypes.byref(n)))
+    return int(n.value)
+
+
+def moe_rope_quantize_per_head(x, positions, inv_freq, interleaved=False, inverse=False,
+                               static_scales=None, codes=None, scales=None, workspace=None,
+                               stream=None):
+    """x [T, nH, D] bf16/f32, positions int32 [T], inv_freq f32 [D/2] (device)
+    -> (E4M3 codes uint8 [T, nH, D], scales f32 [nH])."""
+    T, nH, D = x.shape
+    dev = x.device
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=dev) if codes is None else codes
+    scales = torch.empty(nH, dtype=torch.float32, device=dev) if scales is None else scales
+    if workspace is None:
+        workspace = torch.empty(max(moe_rope_workspace_size(T, nH, D), 16), dtype=torch.uint8,
+                                device=dev)
+    _check(lib().moe_rope_quantize_per_head(
+        _ptr(x), dtype_code(x.dtype), _ptr(positions), _ptr(inv_freq), T, nH, D,
+        int(bool(interleaved)), int(bool(inverse)), _ptr(static_scales), _ptr(codes),
+        _ptr(scales), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return codes, scales
 
 
 @dataclass

@@ -264,3 +264,24 @@ def test_noalloc_forward_rejects_oversized_problem_without_launch():
     with pytest.raises(moe.MoEError) as e:
         moe.moe_fused_forward_noalloc(q, f, f, f, f, al, _Fake(0x7f0100000000), stream=_FakeStream())
     assert e.value.status == moe.MOE_ERR_SHAPE
+
+
+def test_rope_rejects_without_launch():
+    L = moe.lib()
+    f = FAKE
+    ws = 1 << 20
+
+    def call(T=64, nH=32, D=128, dt=moe.MOE_BF16, x=f, codes=f, w=f, wsb=ws):
+        return L.moe_rope_quantize_per_head(x, dt, f, f, T, nH, D, 0, 0, None, codes, f, w, wsb,
+                                            None)
+    assert call(D=100) == moe.MOE_ERR_SHAPE
+    assert call(D=4096) == moe.MOE_ERR_SHAPE
+    assert call(nH=0) == moe.MOE_ERR_SHAPE and call(nH=257) == moe.MOE_ERR_SHAPE
+    assert call(T=-1) == moe.MOE_ERR_SHAPE
+    assert call(dt=moe.MOE_FP8_E4M3) == moe.MOE_ERR_DTYPE
+    assert call(x=None) == moe.MOE_ERR_NULL
+    assert call(codes=ctypes.c_void_p(0x7f0000001008)) == moe.MOE_ERR_ALIGN
+    assert call(wsb=16) == moe.MOE_ERR_WORKSPACE
+    assert call(T=0, x=None) == moe.MOE_OK
+    n = ctypes.c_size_t(0)
+    assert L.moe_rope_workspace_size(8192, 32, 128, ctypes.byref(n)) == moe.MOE_OK and n.value > 0
