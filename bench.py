@@ -53,6 +53,11 @@ def parse():
     ap.add_argument("--router", action="store_true",
                     help="time the router projection fused with the routing "
                          "(moe_route_project_topk) on the workload's activations instead of the layer")
+    ap.add_argument("--rope", action="store_true",
+                    help="time the rotary embedding + per-head E4M3 kernel "
+                         "(moe_rope_quantize_per_head) on x [tokens, 32 heads, 128] bf16 instead of the layer")
+    ap.add_argument("--heads", type=int, default=32)
+    ap.add_argument("--head-dim", type=int, default=128)
     ap.add_argument("--copy-check", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -205,6 +210,110 @@ def router_main(args):
     print(json.dumps(line), flush=True)
 
 
+def rope_main(args):
+    """Rotary position embedding fused with per-head E4M3 quantisation on
+    x [T, heads, head_dim] bf16 ~ N(0, 1), positions 0..T-1, inverse
+    frequencies 10000^(-2i/D).  Each of the K timed steps follows a 512 MiB
+    flush and is bracketed by HIP events on the launch stream.  Algorithmic
+    bytes: x read once, the codes written once, positions, frequencies and
+    scales (the second read of x by the quantising pass is not counted)."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_13_amd import inputs, moe
+
+    moe.lib()  # fail loudly if the HIP library is missing
+    dev = "cuda"
+    T, nH, D = args.tokens, args.heads, args.head_dim
+    x = inputs.make_x(T, nH * D, 4000 + T, torch.bfloat16, device=dev).view(T, nH, D)
+    pos = torch.arange(T, dtype=torch.int32, device=dev)
+    invf = torch.tensor((10000.0 ** (-np.arange(0, D, 2) / D)).astype(np.float32), device=dev)
+    codes = torch.empty(T, nH, D, dtype=torch.uint8, device=dev)
+    scales = torch.empty(nH, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(moe.moe_rope_workspace_size(T, nH, D), 16), dtype=torch.uint8, device=dev)
+
+    def call():
+        moe.moe_rope_quantize_per_head(x, pos, invf, codes=codes, scales=scales, workspace=ws)
+
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        call()
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    st = torch.cuda.current_stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    sev = ev.create(2 * K)
+    torch.cuda.synchronize()
+    for i in range(K):
+        flush.fill_(i & 0xFF)
+        ev.record(sev[2 * i], st.cuda_stream)
+        call()
+        ev.record(sev[2 * i + 1], st.cuda_stream)
+    torch.cuda.synchronize()
+    us = np.array([ev.elapsed_ms(sev[2 * i], sev[2 * i + 1]) for i in range(K)]) * 1e3
+    med = float(np.median(us))
+    # warm, for context: back-to-back calls in one graph
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for _ in range(K):
+                moe.moe_rope_quantize_per_head(x, pos, invf, codes=codes, scales=scales,
+                                               workspace=ws, stream=cap)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    warm_us = (time.perf_counter() - w0) * 1e6 / K
+    del graph, flush
+    n = T * nH * D
+    alg = n * (2 + 1) + T * 4 + (D // 2) * 4 + nH * 4
+    achieved = alg / (med * 1e-6) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "rope_amax_kernel + rope_scale_kernel + rope_quant_kernel" if n > (1 << 18)
+            else "rope_one_kernel",
+            "avg_launch_us": round(float(us.mean()), 2), "algorithmic_bytes_per_launch": int(alg)}
+    cpu = None
+    if args.cpu_sample > 0:
+        import oracle
+
+        S = min(args.cpu_sample, T)
+        xb = inputs.to_numpy_bits(x[:S])
+        pb = pos[:S].cpu().numpy()
+        fb = invf.cpu().numpy()
+        c0 = time.perf_counter()
+        oracle.rope_quant_per_head(xb, pb, fb)
+        once = time.perf_counter() - c0
+        reps = max(1, int(np.ceil(args.cpu_seconds / max(once, 1e-3))))
+        c0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.rope_quant_per_head(xb, pb, fb)
+        wall = time.perf_counter() - c0
+        cpu = {"value": round(S * reps / wall, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {S} tokens as a batch of their own (fp64 rotation, per-head "
+                         f"scales, codes), {reps} passes, {wall:.1f} s wall"}
+    line = {
+        "metric": "rotary embedding + per-head E4M3 quantisation tokens/s",
+        "value": round(T / (med * 1e-6), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(med * 1e-3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; no public dataset or trained weights on the pages)",
+        "config": {"workload": f"rope_fp8 T={T} heads={nH} head_dim={D}", "tokens": T,
+                   "heads": nH, "head_dim": D},
+        "timing": "median of K calls, each after a 512 MiB write that evicts L2 and the MALL, "
+                  "HIP events on the launch stream",
+        "timed": {"median_us": round(med, 2), "p10_us": round(float(np.percentile(us, 10)), 2),
+                  "p90_us": round(float(np.percentile(us, 90)), 2), "steps": K},
+        "roofline": roof, "cpu_baseline": cpu,
+        "warm": {"us_per_call": round(warm_us, 2)},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -214,6 +323,9 @@ def main():
         sys.exit(2)
     if args.router:
         router_main(args)
+        return
+    if args.rope:
+        rope_main(args)
         return
     import numpy as np
     import torch

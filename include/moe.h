@@ -331,12 +331,12 @@ moe_status moe_fused_forward_profiled(
  *            16-byte aligned.
  * positions  device int32 [T], |positions[t]| < 2^24.
  * inv_freq   device f32 [head_dim / 2] (e.g. base^(-2i/D)).
- * static_scales  device f32 [n_heads] or NULL (dynamic).
+ * static_scales  device f32 [n_heads] or NULL (dynamic); normal positive values.
  * codes      device uint8 [T, n_heads, head_dim] (written), 16-byte aligned.
  * scales     device f32 [n_heads] (written: the scales used).
  * workspace  device, >= moe_rope_workspace_size() bytes, 16-byte aligned (no
  *            initialisation, not preserved).
- * Limits: 1 <= n_heads <= 256; head_dim a multiple of 16 in [16, 2048].
+ * Limits: 1 <= n_heads <= 256; head_dim a multiple of 16 in [16, 512].
  * T == 0 is a no-op.  Errors: MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_NULL,
  * MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_HIP; nothing is enqueued on an
  * error.  T is only ever a kernel argument.

@@ -481,8 +481,8 @@ moe_status moe_fused_forward_profiled(
 static moe_status check_rope_dims(int32_t T, int32_t n_heads, int32_t head_dim) {
   if (T < 0) return fail(MOE_ERR_SHAPE, "T=%d must be >= 0", T);
   if (n_heads < 1 || n_heads > 256) return fail(MOE_ERR_SHAPE, "n_heads=%d must be in [1, 256]", n_heads);
-  if (head_dim < 16 || head_dim > 2048 || head_dim % 16)
-    return fail(MOE_ERR_SHAPE, "head_dim=%d must be a multiple of 16 in [16, 2048]", head_dim);
+  if (head_dim < 16 || head_dim > 512 || head_dim % 16)
+    return fail(MOE_ERR_SHAPE, "head_dim=%d must be a multiple of 16 in [16, 512]", head_dim);
   if ((long long)T * n_heads * head_dim > (1LL << 34))
     return fail(MOE_ERR_SHAPE, "T*n_heads*head_dim too large");
   return MOE_OK;

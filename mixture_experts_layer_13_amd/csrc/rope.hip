@@ -15,83 +15,109 @@
 //   (1 when 0) or a static per-head scale; codes E4M3(fl32(y / s_h)).
 // The GPU rotates in fp32 (sincosf of the fp32 angle, fused multiply-adds).
 //
-// Layout of the work: a unit is 16 outputs of one (token, head): 8 pairs of
-// consecutive pair indices.  A workgroup takes TB tokens at a time; their
-// cos/sin values are computed once into LDS and shared by the nH heads.
-//   rope_amax_kernel   rotate, per-head max |y| of its tokens -> partials[wg][h]
-//   rope_scale_kernel  one workgroup: s_h from the partials -> scales[h]
-//   rope_quant_kernel  rotate again (x from L2 / the MALL), codes of y / s_h
+// Layout of the work: one wave takes one token at a time.  A unit is 16
+// outputs of one head of the token (8 pairs of consecutive pair indices);
+// each lane takes units lane, lane + 64, ... of the token, issuing the loads
+// of up to rope_items() units before using any of them.  While they are in
+// flight the lanes compute the token's D/2 cos/sin values (the position is
+// one scalar load, the inverse frequencies sit in registers) into the wave's
+// own LDS row, so no workgroup barrier is needed until the end of a kernel.
+//   rope_amax_kernel   rotate, per-head max |y| of the workgroup's tokens ->
+//                      partials[wg][h]
+//   rope_quant_kernel  every workgroup reduces the partials to s_h, rotates
+//                      again (x from L2 / the MALL) and writes the codes
 //   rope_one_kernel    both passes in one workgroup (small batches: one launch)
 // With static scales only rope_quant_kernel runs.  T is only ever a kernel
 // argument.
+//
+// The codes: fl32(y / s_h) without a division per element, by Markstein's
+// correction step (P. Markstein, IBM J. Res. Dev. 34(1), 1990): with
+// r = fl32(1 / s_h) correctly rounded and q = fl32(y * r), the residual
+// e = y - s_h * q from one fused multiply-add and fl32(q + e * r) give the
+// correctly rounded quotient, except possibly within two ulps of a power of
+// two, where the residual can need one bit more than binary32 holds; powers
+// of two are E4M3 values, not rounding midpoints, so the E4M3 code is that of
+// the correctly rounded quotient in every case.  Quotients beyond 1024 in
+// magnitude keep q (their code saturates whatever the last bits).  The code
+// of the clamped quotient comes from v_cvt_pk_fp8_f32, which rounds to
+// nearest even like the software encoder (checked equal on every E4M3
+// midpoint, its neighbours and a dense sample of the fp32 range).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace moe {
 
-constexpr int kRopeThreads = 256;
-constexpr int kRopeOneThreads = 1024;
-constexpr int kRopeMaxAngles = 1024;  // TB * D/2 per iteration
-constexpr int kRopeMaxGrid = 1024;
+constexpr int kRopeThreads = 1024;
+constexpr int kRopeWaves = kRopeThreads / kWave;
+constexpr int kRopeMaxHalf = 256;                    // D <= 512
+constexpr int kRopeAnglesPerLane = kRopeMaxHalf / kWave;
+constexpr int kRopeMaxGrid = 256;                    // workgroups of a pass (partials per head)
 constexpr int kRopeMaxHeads = 256;
-constexpr long long kRopeOneMax = 1LL << 18;  // elements handled by one workgroup
+constexpr long long kRopeOneMax = 1LL << 15;         // elements handled by one workgroup
+
+// Units per lane and sweep: four with bf16 x, two with f32 x (the same 128
+// bytes of loads in flight per lane).
+template <int XT>
+constexpr int rope_items() {
+  return XT == DT_BF16 ? 4 : 2;
+}
 
 struct RopeArgs {
   const void* x;
   const int32_t* pos;
   const float* inv_freq;
-  int T, nH, D, TB, TB1, inverse;  // TB / TB1: tokens per block (grid / one workgroup)
+  int T, nH, D, inverse;
   const float* static_scales;
   uint8_t* codes;
   float* scales;    // [nH] written
   float* partials;  // [grid][nH]
 };
 
-// Eight consecutive elements of x starting at element i (16-byte aligned).
-template <int XT>
-__device__ __forceinline__ void rope_load8(const void* x, size_t i, float v[8]) {
+// Raw bits of unit g of head h of token t: bf16 x takes two 16-byte loads
+// (p then q), f32 four.  Halves pairing: p holds positions 8g..8g+7 and q the
+// same positions + D/2; interleaved: p and q hold positions 16g..16g+15.
+template <int XT, bool IL>
+__device__ __forceinline__ void rope_load(const RopeArgs& a, int t, int h, int g, i32x4 raw[4]) {
+  const size_t row = ((size_t)t * a.nH + h) * a.D;
+  const size_t ip = row + (IL ? 16 * g : 8 * g);
+  const size_t iq = IL ? ip + 8 : row + (a.D >> 1) + 8 * g;
   if (XT == DT_BF16) {
-    const i32x4 q = ld16(reinterpret_cast<const uint16_t*>(x) + i);
+    raw[0] = ld16(reinterpret_cast<const uint16_t*>(a.x) + ip);
+    raw[1] = ld16(reinterpret_cast<const uint16_t*>(a.x) + iq);
+  } else {
+    raw[0] = ld16(reinterpret_cast<const float*>(a.x) + ip);
+    raw[1] = ld16(reinterpret_cast<const float*>(a.x) + ip + 4);
+    raw[2] = ld16(reinterpret_cast<const float*>(a.x) + iq);
+    raw[3] = ld16(reinterpret_cast<const float*>(a.x) + iq + 4);
+  }
+}
+
+template <int XT>
+__device__ __forceinline__ void rope_unpack8(const i32x4* raw, float v[8]) {
+  if (XT == DT_BF16) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[2 * j] = bf16_bits_to_f32((uint32_t)q[j] & 0xffffu);
-      v[2 * j + 1] = bf16_bits_to_f32((uint32_t)q[j] >> 16);
+      v[2 * j] = bf16_bits_to_f32((uint32_t)raw[0][j] & 0xffffu);
+      v[2 * j + 1] = bf16_bits_to_f32((uint32_t)raw[0][j] >> 16);
     }
   } else {
-    const i32x4 p = ld16(reinterpret_cast<const float*>(x) + i);
-    const i32x4 q = ld16(reinterpret_cast<const float*>(x) + i + 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[j] = __int_as_float(p[j]);
-      v[4 + j] = __int_as_float(q[j]);
+      v[j] = __int_as_float(raw[0][j]);
+      v[4 + j] = __int_as_float(raw[1][j]);
     }
   }
 }
 
-// cos/sin of the angles of tokens [t0, t0 + nt) into cs[tl * D/2 + i].
-__device__ __forceinline__ void rope_angles(const RopeArgs& a, int t0, int nt, float2* cs) {
-  const int half = a.D >> 1;
-  for (int k = threadIdx.x; k < nt * half; k += blockDim.x) {
-    const int tl = k / half, i = k - tl * half;
-    float ang = (float)a.pos[t0 + tl] * a.inv_freq[i];
-    if (a.inverse) ang = -ang;
-    float s, c;
-    sincosf(ang, &s, &c);
-    cs[k] = make_float2(c, s);
-  }
-}
-
-// The 16 outputs of unit g of head h of token t.  Halves pairing: y[0..7]
-// are positions 8g..8g+7, y[8..15] the same positions + D/2.  Interleaved:
-// y[0..15] are positions 16g..16g+15.
+// The 16 outputs of a unit from its raw bits (cs: the token's cos/sin row).
+// Halves pairing: y[0..7] are positions 8g..8g+7, y[8..15] the same + D/2;
+// interleaved: y[0..15] are positions 16g..16g+15.
 template <int XT, bool IL>
-__device__ __forceinline__ void rope_unit(const RopeArgs& a, int t, int h, int g,
-                                          const float2* cs, float y[16]) {
-  const size_t row = ((size_t)t * a.nH + h) * a.D;
+__device__ __forceinline__ void rope_rotate(const i32x4 raw[4], int g, const float2* cs, float y[16]) {
   float p[8], q[8];
+  rope_unpack8<XT>(raw, p);
+  rope_unpack8<XT>(raw + (XT == DT_BF16 ? 1 : 2), q);
   if (IL) {
-    rope_load8<XT>(a.x, row + 16 * g, p);
-    rope_load8<XT>(a.x, row + 16 * g + 8, q);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float u = j < 4 ? p[2 * j] : q[2 * j - 8];
@@ -101,8 +127,6 @@ __device__ __forceinline__ void rope_unit(const RopeArgs& a, int t, int h, int g
       y[2 * j + 1] = __builtin_fmaf(v, c.x, u * c.y);
     }
   } else {
-    rope_load8<XT>(a.x, row + 8 * g, p);
-    rope_load8<XT>(a.x, row + (a.D >> 1) + 8 * g, q);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float2 c = cs[8 * g + j];
@@ -112,12 +136,27 @@ __device__ __forceinline__ void rope_unit(const RopeArgs& a, int t, int h, int g
   }
 }
 
+// fl32(y / s), clamped to +-448, as described at the top (r = fl32(1 / s)).
+__device__ __forceinline__ float rope_quotient(float y, float s, float r) {
+  const float q0 = y * r;
+  const float e = __builtin_fmaf(-q0, s, y);
+  const float q1 = __builtin_fmaf(e, r, q0);
+  const float q = __builtin_fabsf(q0) < 1024.0f ? q1 : q0;
+  return __builtin_fminf(__builtin_fmaxf(q, -448.0f), 448.0f);
+}
+
 template <bool IL>
 __device__ __forceinline__ void rope_store(const RopeArgs& a, int t, int h, int g, const float y[16],
-                                           float s) {
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
+                                           float s, float r) {
+  uint32_t w[4];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) w[j >> 2] |= f32_to_e4m3(y[j] / s) << (8 * (j & 3));
+  for (int j = 0; j < 4; ++j) {
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(rope_quotient(y[4 * j], s, r),
+                                            rope_quotient(y[4 * j + 1], s, r), 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(rope_quotient(y[4 * j + 2], s, r),
+                                        rope_quotient(y[4 * j + 3], s, r), v, true);
+    w[j] = (uint32_t)v;
+  }
   uint8_t* row = a.codes + ((size_t)t * a.nH + h) * a.D;
   if (IL) {
     *reinterpret_cast<uint4*>(row + 16 * g) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -127,106 +166,167 @@ __device__ __forceinline__ void rope_store(const RopeArgs& a, int t, int h, int 
   }
 }
 
-// Pass 1 over this workgroup's token blocks: per-head max |y| into am (LDS,
-// as the bits of non-negative floats, whose integer order is their order).
-// The block's (token, unit) items are spread over the threads.  cs is two
-// buffers of kRopeMaxAngles: a buffer is rewritten two blocks after its use,
-// past a barrier every thread has reached.
-template <int XT, bool IL>
-__device__ __forceinline__ void rope_pass_amax(const RopeArgs& a, int TB, int tb0, int tbstep,
-                                               float2* cs, uint32_t* am) {
-  const int gph = a.D >> 4, upt = a.nH * gph;
-  int it = 0;
-  for (int t0 = tb0 * TB; t0 < a.T; t0 += tbstep * TB, ++it) {
-    const int nt = min(TB, a.T - t0);
-    float2* c = cs + (it & 1) * kRopeMaxAngles;
-    rope_angles(a, t0, nt, c);
-    __syncthreads();
-    for (int k = threadIdx.x; k < nt * upt; k += blockDim.x) {
-      const int tl = k / upt, r = k - tl * upt, h = r / gph, g = r - h * gph;
-      float y[16];
-      rope_unit<XT, IL>(a, t0 + tl, h, g, c + tl * (a.D >> 1), y);
-      float m = 0.0f;
+// Lane state kept for the whole kernel: inv_freq[lane + 64 j].
+struct RopeLane {
+  float invf[kRopeAnglesPerLane];
+};
+
+__device__ __forceinline__ RopeLane rope_lane(const RopeArgs& a) {
+  RopeLane L;
+  const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(y[j]));
-      atomicMax(&am[h], __float_as_uint(m));
+  for (int j = 0; j < kRopeAnglesPerLane; ++j) {
+    const int i = lane + kWave * j;
+    L.invf[j] = i < (a.D >> 1) ? a.inv_freq[i] : 0.0f;
+  }
+  return L;
+}
+
+// cos/sin of token t's D/2 angles into the wave's LDS row cs.
+__device__ __forceinline__ void rope_token_angles(const RopeArgs& a, const RopeLane& L, int t,
+                                                  float2* cs) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const float p = (float)a.pos[t];  // t is uniform over the wave: one scalar load
+#pragma unroll
+  for (int j = 0; j < kRopeAnglesPerLane; ++j) {
+    const int i = lane + kWave * j;
+    if (i < (a.D >> 1)) {
+      float ang = p * L.invf[j];
+      if (a.inverse) ang = -ang;
+      float s, c;
+      sincosf(ang, &s, &c);
+      cs[i] = make_float2(c, s);
     }
   }
 }
 
-template <int XT, bool IL>
-__device__ __forceinline__ void rope_pass_quant(const RopeArgs& a, int TB, int tb0, int tbstep,
-                                                float2* cs, const float* sc) {
+// Orders a wave's own LDS writes before its later reads (and reads before
+// later writes): the wave's lanes run in lockstep, so a wave-scope fence
+// around a wave barrier suffices.
+__device__ __forceinline__ void rope_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One pass of a wave over its tokens (w0, w0 + wstep, ...).  QUANT = false:
+// per-head max |y| into am (LDS, as the bits of non-negative floats, whose
+// integer order is their order).  QUANT = true: the codes of y / sc[h]
+// (rc[h] = fl32(1 / sc[h])).  cs is the wave's own LDS row.
+template <int XT, bool IL, bool QUANT>
+__device__ __forceinline__ void rope_wave_pass(const RopeArgs& a, const RopeLane& L, int w0,
+                                               int wstep, float2* cs, uint32_t* am,
+                                               const float* sc, const float* rc) {
+  constexpr int NI = rope_items<XT>();
+  const int lane = threadIdx.x & (kWave - 1);
   const int gph = a.D >> 4, upt = a.nH * gph;
-  int it = 0;
-  for (int t0 = tb0 * TB; t0 < a.T; t0 += tbstep * TB, ++it) {
-    const int nt = min(TB, a.T - t0);
-    float2* c = cs + (it & 1) * kRopeMaxAngles;
-    rope_angles(a, t0, nt, c);
-    __syncthreads();
-    for (int k = threadIdx.x; k < nt * upt; k += blockDim.x) {
-      const int tl = k / upt, r = k - tl * upt, h = r / gph, g = r - h * gph;
-      float y[16];
-      rope_unit<XT, IL>(a, t0 + tl, h, g, c + tl * (a.D >> 1), y);
-      rope_store<IL>(a, t0 + tl, h, g, y, sc[h]);
+  for (int t = w0; t < a.T; t += wstep) {
+    for (int base = 0; base < upt; base += NI * kWave) {
+      int hs[NI], gs[NI];
+      bool live[NI];
+      i32x4 raw[NI][4];
+#pragma unroll
+      for (int s = 0; s < NI; ++s) {  // every load first
+        const int r = base + lane + s * kWave;
+        live[s] = r < upt;
+        const int rr = live[s] ? r : 0;  // a unit past the token reads unit 0
+        hs[s] = rr / gph;
+        gs[s] = rr - hs[s] * gph;
+        rope_load<XT, IL>(a, t, hs[s], gs[s], raw[s]);
+      }
+      if (base == 0) {
+        rope_token_angles(a, L, t, cs);
+        rope_wave_sync();
+      }
+#pragma unroll
+      for (int s = 0; s < NI; ++s) {
+        float y[16];
+        rope_rotate<XT, IL>(raw[s], gs[s], cs, y);
+        if (QUANT) {
+          if (live[s]) rope_store<IL>(a, t, hs[s], gs[s], y, sc[hs[s]], rc[hs[s]]);
+        } else {
+          float m = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(y[j]));
+          if (live[s]) atomicMax(&am[hs[s]], __float_as_uint(m));
+        }
+      }
     }
+    rope_wave_sync();  // the next token's angles overwrite cs
   }
 }
 
 template <int XT, bool IL>
 __global__ __launch_bounds__(kRopeThreads) void rope_amax_kernel(RopeArgs a) {
-  __shared__ float2 cs[2 * kRopeMaxAngles];
+  __shared__ float2 cs[kRopeWaves][kRopeMaxHalf];
   __shared__ uint32_t am[kRopeMaxHeads];
   for (int h = threadIdx.x; h < a.nH; h += blockDim.x) am[h] = 0u;
-  // (the first barrier inside the pass orders these stores before any atomic)
-  rope_pass_amax<XT, IL>(a, a.TB, blockIdx.x, gridDim.x, cs, am);
+  const RopeLane L = rope_lane(a);
+  __syncthreads();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), waves = blockDim.x / kWave;
+  rope_wave_pass<XT, IL, false>(a, L, blockIdx.x * waves + wave, gridDim.x * waves, cs[wave], am,
+                                nullptr, nullptr);
   __syncthreads();
   for (int h = threadIdx.x; h < a.nH; h += blockDim.x)
     a.partials[(size_t)blockIdx.x * a.nH + h] = __uint_as_float(am[h]);
 }
 
-// One workgroup: s_h = fl32(max of the partials / 448), 1 when 0.
-__global__ __launch_bounds__(kRopeOneThreads) void rope_scale_kernel(RopeArgs a, int nparts) {
-  __shared__ uint32_t am[kRopeMaxHeads];
-  for (int h = threadIdx.x; h < a.nH; h += blockDim.x) am[h] = 0u;
-  __syncthreads();
-  const int per = blockDim.x / a.nH;  // >= 4: nH <= 256
-  if ((int)threadIdx.x < per * a.nH) {
-    const int h = threadIdx.x % a.nH, c = threadIdx.x / a.nH;
-    float m = 0.0f;
-    for (int p = c; p < nparts; p += per) m = fmaxf(m, a.partials[(size_t)p * a.nH + h]);
-    atomicMax(&am[h], __float_as_uint(m));
+// s_h and its reciprocal into sc / rc from the nparts partials (static
+// scales when given); block 0 writes the scales out.  Ends with a barrier.
+__device__ __forceinline__ void rope_scales(const RopeArgs& a, int nparts, uint32_t* am, float* sc,
+                                            float* rc) {
+  if (!a.static_scales) {
+    for (int h = threadIdx.x; h < a.nH; h += blockDim.x) am[h] = 0u;
+    __syncthreads();
+    const int per = blockDim.x / a.nH;  // >= 4: nH <= 256
+    if ((int)threadIdx.x < per * a.nH) {
+      const int h = threadIdx.x % a.nH;
+      float m = 0.0f;
+      for (int p = threadIdx.x / a.nH; p < nparts; p += per)
+        m = fmaxf(m, a.partials[(size_t)p * a.nH + h]);
+      atomicMax(&am[h], __float_as_uint(m));
+    }
+    __syncthreads();
   }
-  __syncthreads();
   for (int h = threadIdx.x; h < a.nH; h += blockDim.x) {
-    const float m = __uint_as_float(am[h]);
-    a.scales[h] = (m == 0.0f) ? 1.0f : m / 448.0f;
+    float s;
+    if (a.static_scales) {
+      s = a.static_scales[h];
+    } else {
+      const float m = __uint_as_float(am[h]);
+      s = (m == 0.0f) ? 1.0f : m / 448.0f;
+    }
+    sc[h] = s;
+    rc[h] = 1.0f / s;
+    if (blockIdx.x == 0) a.scales[h] = s;
   }
+  __syncthreads();
 }
 
-// Pass 2; scales from a.static_scales when given (block 0 copies them to
-// a.scales), else from a.scales (written by rope_scale_kernel).
 template <int XT, bool IL>
-__global__ __launch_bounds__(kRopeThreads) void rope_quant_kernel(RopeArgs a) {
-  __shared__ float2 cs[2 * kRopeMaxAngles];
-  __shared__ float sc[kRopeMaxHeads];
-  const float* src = a.static_scales ? a.static_scales : a.scales;
-  for (int h = threadIdx.x; h < a.nH; h += blockDim.x) {
-    sc[h] = src[h];
-    if (a.static_scales && blockIdx.x == 0) a.scales[h] = src[h];
-  }
-  // (the first barrier inside the pass orders sc before its reads)
-  rope_pass_quant<XT, IL>(a, a.TB, blockIdx.x, gridDim.x, cs, sc);
+__global__ __launch_bounds__(kRopeThreads) void rope_quant_kernel(RopeArgs a, int nparts) {
+  __shared__ float2 cs[kRopeWaves][kRopeMaxHalf];
+  __shared__ uint32_t am[kRopeMaxHeads];
+  __shared__ float sc[kRopeMaxHeads], rc[kRopeMaxHeads];
+  const RopeLane L = rope_lane(a);
+  rope_scales(a, nparts, am, sc, rc);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), waves = blockDim.x / kWave;
+  rope_wave_pass<XT, IL, true>(a, L, blockIdx.x * waves + wave, gridDim.x * waves, cs[wave],
+                               nullptr, sc, rc);
 }
 
 // Both passes in one workgroup (x is read the second time from L2).
 template <int XT, bool IL>
-__global__ __launch_bounds__(kRopeOneThreads) void rope_one_kernel(RopeArgs a) {
-  __shared__ float2 cs[2 * kRopeMaxAngles];
+__global__ __launch_bounds__(kRopeThreads) void rope_one_kernel(RopeArgs a) {
+  __shared__ float2 cs[kRopeWaves][kRopeMaxHalf];
   __shared__ uint32_t am[kRopeMaxHeads];
-  __shared__ float sc[kRopeMaxHeads];
+  __shared__ float sc[kRopeMaxHeads], rc[kRopeMaxHeads];
   for (int h = threadIdx.x; h < a.nH; h += blockDim.x) am[h] = 0u;
-  if (!a.static_scales) rope_pass_amax<XT, IL>(a, a.TB1, 0, 1, cs, am);
+  const RopeLane L = rope_lane(a);
+  __syncthreads();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), waves = blockDim.x / kWave;
+  if (!a.static_scales)
+    rope_wave_pass<XT, IL, false>(a, L, wave, waves, cs[wave], am, nullptr, nullptr);
   __syncthreads();
   for (int h = threadIdx.x; h < a.nH; h += blockDim.x) {
     float s;
@@ -237,10 +337,11 @@ __global__ __launch_bounds__(kRopeOneThreads) void rope_one_kernel(RopeArgs a) {
       s = (m == 0.0f) ? 1.0f : m / 448.0f;
     }
     sc[h] = s;
+    rc[h] = 1.0f / s;
     a.scales[h] = s;
   }
-  // every thread is past the last use of both cs buffers (barrier above)
-  rope_pass_quant<XT, IL>(a, a.TB1, 0, 1, cs, sc);
+  __syncthreads();
+  rope_wave_pass<XT, IL, true>(a, L, wave, waves, cs[wave], nullptr, sc, rc);
 }
 
 size_t rope_workspace_bytes(int T, int nH, int D) {
@@ -250,23 +351,25 @@ size_t rope_workspace_bytes(int T, int nH, int D) {
 }
 
 template <int XT, bool IL>
-static int rope_launch(RopeArgs a, hipStream_t st) {
+static int rope_launch(const RopeArgs& a, hipStream_t st) {
   const long long n = (long long)a.T * a.nH * a.D;
   if (n <= kRopeOneMax) {
-    hipLaunchKernelGGL((rope_one_kernel<XT, IL>), dim3(1), dim3(kRopeOneThreads), 0, st, a);
+    hipLaunchKernelGGL((rope_one_kernel<XT, IL>), dim3(1), dim3(kRopeThreads), 0, st, a);
     return (int)hipGetLastError();
   }
-  const int blocks = (a.T + a.TB - 1) / a.TB;
-  const int g = blocks < kRopeMaxGrid ? blocks : kRopeMaxGrid;
+  // one token per wave at a time: enough workgroups to give every wave a
+  // token, at most one per CU (and kRopeMaxGrid)
+  long long g = ((long long)a.T + kRopeWaves - 1) / kRopeWaves;
+  const int cus = device_cu_count();
+  if (g > cus) g = cus;
+  if (g > kRopeMaxGrid) g = kRopeMaxGrid;
   if (!a.static_scales) {
-    hipLaunchKernelGGL((rope_amax_kernel<XT, IL>), dim3(g), dim3(kRopeThreads), 0, st, a);
-    int err = (int)hipGetLastError();
-    if (err) return err;
-    hipLaunchKernelGGL(rope_scale_kernel, dim3(1), dim3(kRopeOneThreads), 0, st, a, g);
-    err = (int)hipGetLastError();
+    hipLaunchKernelGGL((rope_amax_kernel<XT, IL>), dim3((unsigned)g), dim3(kRopeThreads), 0, st, a);
+    const int err = (int)hipGetLastError();
     if (err) return err;
   }
-  hipLaunchKernelGGL((rope_quant_kernel<XT, IL>), dim3(g), dim3(kRopeThreads), 0, st, a);
+  hipLaunchKernelGGL((rope_quant_kernel<XT, IL>), dim3((unsigned)g), dim3(kRopeThreads), 0, st, a,
+                     (int)g);
   return (int)hipGetLastError();
 }
 
@@ -285,17 +388,6 @@ int launch_rope_quant(const void* x, int xt, const int32_t* pos, const float* in
   a.codes = codes;
   a.scales = scales;
   a.partials = reinterpret_cast<float*>(ws);
-  // tokens per block: about four units per thread, the block's angles in one
-  // LDS buffer
-  const int upt = nH * (D / 16);
-  auto tokens_per_block = [&](int threads) {
-    int tb = (4 * threads) / upt;
-    if (tb < 1) tb = 1;
-    if (tb > kRopeMaxAngles / (D / 2)) tb = kRopeMaxAngles / (D / 2);
-    return tb;
-  };
-  a.TB = tokens_per_block(kRopeThreads);
-  a.TB1 = tokens_per_block(kRopeOneThreads);
   if (xt == DT_BF16)
     return interleaved ? rope_launch<DT_BF16, true>(a, st) : rope_launch<DT_BF16, false>(a, st);
   return interleaved ? rope_launch<DT_F32, true>(a, st) : rope_launch<DT_F32, false>(a, st);

@@ -275,7 +275,7 @@ def test_rope_rejects_without_launch():
         return L.moe_rope_quantize_per_head(x, dt, f, f, T, nH, D, 0, 0, None, codes, f, w, wsb,
                                             None)
     assert call(D=100) == moe.MOE_ERR_SHAPE
-    assert call(D=4096) == moe.MOE_ERR_SHAPE
+    assert call(D=528) == moe.MOE_ERR_SHAPE
     assert call(nH=0) == moe.MOE_ERR_SHAPE and call(nH=257) == moe.MOE_ERR_SHAPE
     assert call(T=-1) == moe.MOE_ERR_SHAPE
     assert call(dt=moe.MOE_FP8_E4M3) == moe.MOE_ERR_DTYPE

@@ -91,7 +91,8 @@ CASES = [
     ("grid_T1000_H32_D128", 1000, 32, 128, torch.bfloat16, False, False, "arange"),
     ("grid_T777_H12_D80_interleaved_inverse", 777, 12, 80, torch.bfloat16, True, True, "random"),
     ("grid_T513_H256_D16", 513, 256, 16, torch.bfloat16, False, False, "random"),
-    ("grid_T300_H1_D2048_f32", 300, 1, 2048, torch.float32, False, True, "random"),
+    ("grid_T300_H2_D512_f32", 300, 2, 512, torch.float32, False, True, "random"),
+    ("grid_T2000_H40_D96", 2000, 40, 96, torch.bfloat16, False, False, "random"),
     ("prefill_T8192_H32_D128", 8192, 32, 128, torch.bfloat16, False, False, "arange"),
 ]
 
