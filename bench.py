@@ -58,6 +58,8 @@ def parse():
                          "(moe_rope_quantize_per_head) on x [tokens, 32 heads, 128] bf16 instead of the layer")
     ap.add_argument("--heads", type=int, default=32)
     ap.add_argument("--head-dim", type=int, default=128)
+    ap.add_argument("--persistent", action="store_true",
+                    help="E4M3 decode: run the forward as one launch (moe_fused_forward_persistent)")
     ap.add_argument("--copy-check", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -339,7 +341,8 @@ def main():
     d = inputs.make_inputs(wl, T, device=dev)
     H, I, E, k = d["H"], d["I"], d["E"], d["topk"]
     layer = moe.FusedMoE(T, H, I, E, k, d["w13"], d["w2"], d["w13_scale"], d["w2_scale"],
-                         a_dtype=wl.x_dtype, out_dtype=wl.out_dtype, device=dev)
+                         a_dtype=wl.x_dtype, out_dtype=wl.out_dtype, device=dev,
+                         persistent=args.persistent)
     x, logits = d["x"], d["logits"]
 
     ev = HipEvents()
@@ -361,7 +364,15 @@ def main():
     for i in range(K):
         flush.fill_(i & 0xFF)
         ev.record(sev[2 * i], st.cuda_stream)
-        layer(x, logits, events=kev[4 * i: 4 * i + 4])
+        if args.persistent:  # the one launch of the forward between the kernel events
+            layer.route(logits)
+            ev.record(kev[4 * i], st.cuda_stream)
+            layer.forward(x)
+            ev.record(kev[4 * i + 1], st.cuda_stream)
+            ev.record(kev[4 * i + 2], st.cuda_stream)
+            ev.record(kev[4 * i + 3], st.cuda_stream)
+        else:
+            layer(x, logits, events=kev[4 * i: 4 * i + 4])
         ev.record(sev[2 * i + 1], st.cuda_stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t0
@@ -433,6 +444,10 @@ def main():
     stream_path = T <= 64
     hbm_bound = (flops / op_bytes) < 300.0
 
+    if args.persistent:
+        # the dominant (only) kernel is the whole forward: its bytes are the
+        # op's, less the routing's logits and ids, which the routing launch reads
+        g1_bytes = op_bytes - T * E * 4 - T * k * 8
     if hbm_bound:
         achieved = g1_bytes / (g1_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -444,7 +459,9 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
     ring = stream_path and wl.w_dtype in ("bf16", "e4m3") and (H * bw) % 512 == 0
-    if stream_path:  # the gate/up instantiation of the persistent expert ring
+    if args.persistent:
+        roof["kernel"] = "fused_decode_kernel"
+    elif stream_path:  # the gate/up instantiation of the persistent expert ring
         roof["kernel"] = "ring_gemm_kernel<W, NCB, 4, WPC, true>" if ring else "gemm1_stream_kernel"
     elif wl.w_dtype in ("bf16", "e4m3"):  # prefill kernels: 256 x 256 tiles with 256-row blocks
         roof["kernel"] = "pfq_gemm_kernel" if layer.block_m == 256 else "pf_gemm_kernel"
@@ -453,7 +470,7 @@ def main():
     roof["avg_launch_us"] = round(g1_ms * 1e3, 2)
     roof["algorithmic_bytes_per_launch"] = int(g1_bytes)
     src_sha = kernel_source_sha()
-    key = f"{args.workload}:T{T}"
+    key = f"{args.workload}:T{T}" + (":persistent" if args.persistent else "")
     if os.path.exists(PMC_FILE):
         rec = json.load(open(PMC_FILE)).get(key)
         if rec and rec.get("gemm_source_sha256") == src_sha:
@@ -532,10 +549,11 @@ def main():
         "config": {"workload": f"{args.workload} T={T} H={H} I={I} E={E} top-{k}",
                    "tokens": T, "hidden": H, "intermediate": I, "experts": E, "topk": k,
                    "active_experts": U, "block_m": layer.block_m,
-                   "kernel_family": "stream" if stream_path else "tile"},
+                   "kernel_family": ("one launch" if args.persistent else
+                                     "stream" if stream_path else "tile")},
         "op_hbm_gbps": round(op_bytes / (ms_step * 1e-3) / 1e9, 1),
         "op_tflops": round(flops / (ms_step * 1e-3) / 1e12, 3),
-        "down_gemm_avg_launch_us": round(g2_ms * 1e3, 2),
+        "down_gemm_avg_launch_us": None if args.persistent else round(g2_ms * 1e3, 2),
         "timing": "median of K steps, each after a 512 MiB write that evicts L2 and the MALL, "
                   "each timed with HIP events on the launch stream; GEMM durations from the "
                   "library's events around its launches inside the same steps",

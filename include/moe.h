@@ -293,6 +293,47 @@ moe_status moe_fused_forward_noalloc(
     const int32_t* num_padded, void* out, void* stream);
 
 /*
+ * moe_fused_forward for E4M3 decode batches in one kernel launch: the
+ * pages' single hardware pass of the FP8 path, in which scaling, the expert
+ * GEMMs and the aggregation run as one fused step instead of discrete
+ * kernels with HBM round trips in between ([post], "Backend routing for FP8
+ * tensor quantization"; "Amazon SageMaker AI 上的 MoE 内核工程优化实践",
+ * "Triton 后端路由").  The same computation as moe_fused_forward, with its
+ * arguments and errors, and the same result bit for bit (every step is done
+ * in the same arithmetic).  One persistent grid of two workgroups per CU runs
+ * the steps as phases separated by grid-wide barriers: the activation scale
+ * and codes, gate/up with SiLU * up, the scale and codes of h, the down
+ * projection, and the weighted combine, which the workgroup finishing the
+ * last expert block of each 32-row output block performs.  After the
+ * workspace arguments:
+ * sync       device, >= MOE_FUSED_SYNC_BYTES bytes, 128-byte aligned: the
+ *            barrier words.  Zero it once before the first call (every call
+ *            leaves it in a state the next call starts from); keep one per
+ *            stream: calls that overlap in time on one sync buffer race.
+ *            After a call, the 32-bit word at byte offset
+ *            MOE_FUSED_SYNC_ERROR_OFFSET is nonzero if a grid-wide wait gave
+ *            up (after about a second: the grid's workgroups could not all
+ *            be resident at once, e.g. when another kernel held the CUs);
+ *            that call's output is then undefined and the buffer must be
+ *            zeroed again.
+ * Limits beyond moe_fused_forward's: w_dtype MOE_FP8_E4M3, a_dtype bf16 or
+ * f32, 1 <= M <= 64 (M == 0 is a no-op), p->block_m == 16, and byte
+ * offsets of the per-pair buffers below 4 GiB; otherwise
+ * MOE_ERR_UNSUPPORTED.  MOE_ERR_HIP also when the device cannot hold two
+ * workgroups per CU of this kernel.
+ */
+#define MOE_FUSED_SYNC_BYTES 32768
+#define MOE_FUSED_SYNC_ERROR_OFFSET 128
+moe_status moe_fused_forward_persistent(
+    const moe_problem* p, const void* a, const void* w13, const void* w2,
+    const float* w13_scale, const float* w2_scale, const float* a1_scale,
+    const float* a2_scale, const float* topk_weights,
+    const int32_t* sorted_pair_ids, const int32_t* block_expert_ids,
+    const int32_t* expert_offsets, const int32_t* pair_pos,
+    const int32_t* num_padded, void* out, void* workspace,
+    size_t workspace_bytes, void* sync, size_t sync_bytes, void* stream);
+
+/*
  * moe_fused_forward with timing events: the same computation, arguments and
  * errors, and in addition hipEventRecord of events[0] / events[1] (hipEvent_t
  * passed as void*) on `stream` right before and after the gate/up GEMM

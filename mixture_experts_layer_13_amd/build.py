@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libmoe.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["moe_api.cpp", "route.hip", "route_project.hip", "align.hip", "quant.hip", "gemm.hip", "ring.hip", "prefill.hip", "prefill2.hip", "rope.hip"]
+SOURCES = ["moe_api.cpp", "route.hip", "route_project.hip", "align.hip", "quant.hip", "gemm.hip", "ring.hip", "prefill.hip", "prefill2.hip", "rope.hip", "fused.hip"]
 
 FLAGS = ["-O3", "--offload-arch=gfx950", "-fPIC", "-std=c++17", "-Wall",
          "-Wno-unused-function", "-fhip-fp32-correctly-rounded-divide-sqrt",

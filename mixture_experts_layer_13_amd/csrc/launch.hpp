@@ -124,6 +124,15 @@ int launch_gemm2_pfq(const GemmArgs& a, hipStream_t stream);
 int launch_gemm1_tile(const GemmArgs& a, hipStream_t stream);
 int launch_gemm2_tile(const GemmArgs& a, hipStream_t stream);
 int launch_combine(const GemmArgs& a, hipStream_t stream);
+
+// Single-launch decode forward (fused.hip): E4M3 weights, a.x the bf16 or
+// fp32 activations, a.h fp32 h, a.hq its codes, a.y per-pair rows, xq the
+// codes of x, sync the zero-initialised synchronisation words
+// (fused_sync_bytes()).
+size_t fused_sync_bytes();
+bool fused_decode_applies(const GemmArgs& a);
+int launch_fused_decode(const GemmArgs& a, uint8_t* xq, uint32_t* sync, const float* a1_scale,
+                        const float* a2_scale, hipStream_t stream);
 int launch_cast_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t stream);
 
 // Compute units of the current device (queried once per device).

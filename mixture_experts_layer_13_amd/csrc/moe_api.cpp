@@ -282,10 +282,18 @@ moe_status fused_forward(const moe_problem* p, const void* a, const void* w13, c
                          const int32_t* sorted_pair_ids, const int32_t* block_expert_ids,
                          const int32_t* expert_offsets, const int32_t* pair_pos,
                          const int32_t* num_padded, void* out, void* workspace,
-                         size_t workspace_bytes, void* stream, void* const* events) {
+                         size_t workspace_bytes, void* stream, void* const* events,
+                         bool persistent = false, void* sync = nullptr, size_t sync_bytes = 0) {
   moe_status s = check_problem(p);
   if (s) return s;
   if (p->M == 0) return ok();
+  if (persistent) {
+    if (!sync) return fail(MOE_ERR_NULL, "sync is NULL");
+    if (!aligned(sync, 128)) return fail(MOE_ERR_ALIGN, "sync must be 128-byte aligned");
+    if (sync_bytes < MOE_FUSED_SYNC_BYTES)
+      return fail(MOE_ERR_WORKSPACE, "sync buffer of %d bytes needed, %zu given",
+                  (int)MOE_FUSED_SYNC_BYTES, sync_bytes);
+  }
   const bool fp8 = p->w_dtype == MOE_FP8_E4M3;
   if (!a || !w13 || !w2 || !topk_weights || !sorted_pair_ids || !block_expert_ids ||
       !expert_offsets || !pair_pos || !num_padded || !out || !workspace)
@@ -351,6 +359,19 @@ moe_status fused_forward(const moe_problem* p, const void* a, const void* w13, c
   g.out = out;
 
   int err = 0;
+  if (persistent) {
+    g.x = a;
+    g.xt = p->a_dtype;
+    g.hq = ws + L.hq;
+    if (!moe::fused_decode_applies(g))
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "the one-launch forward needs E4M3 weights, bf16/f32 activations, "
+                  "1 <= M <= 64, block_m 16 and per-pair buffers under 4 GiB");
+    err = moe::launch_fused_decode(g, (uint8_t*)(ws + L.xq), (uint32_t*)sync, a1_scale, a2_scale,
+                                   st);
+    if (err) return hip_status(err, "one-launch forward");
+    return ok();
+  }
   if (fp8) {
     err = moe::launch_quant_x(a, p->a_dtype, (size_t)p->M * p->K, a1_scale,
                               (float*)(ws + L.partials), (uint8_t*)(ws + L.xq), scal + 0,
@@ -476,6 +497,19 @@ moe_status moe_fused_forward_profiled(
   return fused_forward(p, a, w13, w2, w13_scale, w2_scale, a1_scale, a2_scale, topk_weights,
                        sorted_pair_ids, block_expert_ids, expert_offsets, pair_pos, num_padded,
                        out, workspace, workspace_bytes, stream, events);
+}
+
+moe_status moe_fused_forward_persistent(
+    const moe_problem* p, const void* a, const void* w13, const void* w2,
+    const float* w13_scale, const float* w2_scale, const float* a1_scale, const float* a2_scale,
+    const float* topk_weights, const int32_t* sorted_pair_ids, const int32_t* block_expert_ids,
+    const int32_t* expert_offsets, const int32_t* pair_pos, const int32_t* num_padded, void* out,
+    void* workspace, size_t workspace_bytes, void* sync, size_t sync_bytes, void* stream) {
+  static_assert(MOE_FUSED_SYNC_ERROR_OFFSET == 128, "error word offset");
+  if (moe::fused_sync_bytes() > MOE_FUSED_SYNC_BYTES) return fail(MOE_ERR_UNSUPPORTED, "sync size");
+  return fused_forward(p, a, w13, w2, w13_scale, w2_scale, a1_scale, a2_scale, topk_weights,
+                       sorted_pair_ids, block_expert_ids, expert_offsets, pair_pos, num_padded,
+                       out, workspace, workspace_bytes, stream, nullptr, true, sync, sync_bytes);
 }
 
 static moe_status check_rope_dims(int32_t T, int32_t n_heads, int32_t head_dim) {

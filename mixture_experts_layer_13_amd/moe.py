@@ -20,10 +20,13 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_align_capacity", "moe_workspace_size",
            "moe_route_topk", "moe_align_permute", "moe_fused_forward", "moe_quantize_act",
            "moe_fused_forward_profiled", "moe_fused_forward_noalloc", "moe_route_align", "moe_route_project_topk",
-           "moe_route_project_workspace_size", "moe_rope_quantize_per_head", "moe_rope_workspace_size")
+           "moe_route_project_workspace_size", "moe_rope_quantize_per_head", "moe_rope_workspace_size",
+           "moe_fused_forward_persistent")
 MOE_QUANT_WORKSPACE_BYTES = 8192
 MOE_WORKSPACE_SCALES_OFFSET = 4096
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
+MOE_FUSED_SYNC_BYTES = 32768
+MOE_FUSED_SYNC_ERROR_OFFSET = 128
 
 
 class MoEError(RuntimeError):
@@ -69,6 +72,9 @@ def lib():
         L.moe_fused_forward_profiled.restype = ctypes.c_int
         L.moe_fused_forward_noalloc.argtypes = [ctypes.POINTER(moe_problem)] + [vp] * 15
         L.moe_fused_forward_noalloc.restype = ctypes.c_int
+        L.moe_fused_forward_persistent.argtypes = ([ctypes.POINTER(moe_problem)] + [vp] * 15 +
+                                                   [sz, vp, sz, vp])
+        L.moe_fused_forward_persistent.restype = ctypes.c_int
         L.moe_route_align.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                       vp, sz, vp]
         L.moe_route_align.restype = ctypes.c_int
@@ -290,6 +296,34 @@ def moe_fused_forward(problem, x, w13, w2, topk_weights, alignment, out, workspa
     return out
 
 
+def alloc_fused_sync(device="cuda"):
+    """A zeroed synchronisation buffer for moe_fused_forward_persistent (one
+    per stream; every call leaves it ready for the next)."""
+    return torch.zeros(MOE_FUSED_SYNC_BYTES, dtype=torch.uint8, device=device)
+
+
+def fused_sync_error(sync):
+    """The error word of a synchronisation buffer (nonzero: a grid-wide wait
+    of an earlier call gave up); reads the device, so it synchronises."""
+    o = MOE_FUSED_SYNC_ERROR_OFFSET
+    return int(sync[o:o + 4].view(torch.int32).item())
+
+
+def moe_fused_forward_persistent(problem, x, w13, w2, topk_weights, alignment, out, workspace,
+                                 sync, w13_scale=None, w2_scale=None, a1_scale=None,
+                                 a2_scale=None, stream=None):
+    """moe_fused_forward for E4M3 decode batches in one kernel launch; sync is
+    a zero-initialised MOE_FUSED_SYNC_BYTES buffer (alloc_fused_sync)."""
+    _check(lib().moe_fused_forward_persistent(
+        ctypes.byref(problem), _ptr(x), _ptr(w13), _ptr(w2), _ptr(w13_scale), _ptr(w2_scale),
+        _ptr(a1_scale), _ptr(a2_scale), _ptr(topk_weights), _ptr(alignment.sorted_pair_ids),
+        _ptr(alignment.block_expert_ids), _ptr(alignment.expert_offsets),
+        _ptr(alignment.pair_pos), _ptr(alignment.num_padded), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(sync),
+        sync.numel() * sync.element_size(), _stream(stream)))
+    return out
+
+
 class FusedMoE:
     """The three calls with their buffers allocated once for a fixed maximum
     M (route -> align -> forward).  Buffers are reused between calls, so
@@ -298,7 +332,8 @@ class FusedMoE:
 
     def __init__(self, M, K, N, E, topk, w13, w2, w13_scale=None, w2_scale=None,
                  block_m=None, a_dtype=torch.bfloat16, out_dtype=torch.bfloat16,
-                 renormalize=True, a1_scale=None, a2_scale=None, device="cuda"):
+                 renormalize=True, a1_scale=None, a2_scale=None, device="cuda",
+                 persistent=False):
         if block_m is None:
             # alignment block: 16 rows for decode-sized batches (the stream and
             # ring kernels), 256 once the experts average 512 rows or more (the
@@ -315,6 +350,9 @@ class FusedMoE:
         self.topk_weights = torch.empty(M, topk, dtype=torch.float32, device=device)
         self.alignment = alloc_alignment(M, topk, E, block_m, device)
         self.out = torch.empty(M, K, dtype=out_dtype, device=device)
+        # persistent: the forward runs as one launch (moe_fused_forward_persistent)
+        self.persistent = persistent
+        self.sync = alloc_fused_sync(device) if persistent else None
 
     def act_scales(self):
         """Device view of the (s_x, s_h) fp32 pair that the last E4M3 forward
@@ -323,9 +361,21 @@ class FusedMoE:
         return self.workspace[o:o + 8].view(torch.float32)
 
     def __call__(self, x, logits, stream=None, events=None):
+        self.route(logits, stream)
+        return self.forward(x, stream, events)
+
+    def route(self, logits, stream=None):
         moe_route_align(logits, self.topk, self.renormalize, self.block_m, self.workspace,
                         self.topk_ids, self.topk_weights, self.alignment, stream)
-        moe_fused_forward(self.problem, x, self.w13, self.w2, self.topk_weights, self.alignment,
-                          self.out, self.workspace, self.w13_scale, self.w2_scale,
-                          self.a1_scale, self.a2_scale, stream, events)
+
+    def forward(self, x, stream=None, events=None):
+        if self.persistent:
+            moe_fused_forward_persistent(self.problem, x, self.w13, self.w2, self.topk_weights,
+                                         self.alignment, self.out, self.workspace, self.sync,
+                                         self.w13_scale, self.w2_scale, self.a1_scale,
+                                         self.a2_scale, stream)
+        else:
+            moe_fused_forward(self.problem, x, self.w13, self.w2, self.topk_weights,
+                              self.alignment, self.out, self.workspace, self.w13_scale,
+                              self.w2_scale, self.a1_scale, self.a2_scale, stream, events)
         return self.out

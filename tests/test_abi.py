@@ -285,3 +285,29 @@ def test_rope_rejects_without_launch():
     assert call(T=0, x=None) == moe.MOE_OK
     n = ctypes.c_size_t(0)
     assert L.moe_rope_workspace_size(8192, 32, 128, ctypes.byref(n)) == moe.MOE_OK and n.value > 0
+
+
+def test_persistent_forward_rejects_without_launch():
+    """Argument checks of moe_fused_forward_persistent, all decided on the
+    host before anything is enqueued (fake device addresses, no GPU)."""
+    L = moe.lib()
+    f = FAKE
+    bf, e4 = moe.MOE_BF16, moe.MOE_FP8_E4M3
+
+    def call(M=8, w=e4, bm=16, a=bf, sync=0x7f0000200000, sync_bytes=moe.MOE_FUSED_SYNC_BYTES,
+             ws_bytes=1 << 30):
+        p = moe.moe_problem(M, 4096, 1024, 64, 8, bm, a, w, bf)
+        sc = f if w == e4 else None
+        return L.moe_fused_forward_persistent(ctypes.byref(p), f, f, f, sc, sc, None, None, f, f,
+                                              f, f, f, f, ctypes.c_void_p(0x7f0100000000), f,
+                                              ws_bytes, ctypes.c_void_p(sync) if sync else None,
+                                              sync_bytes, None)
+    assert call(sync=0) == moe.MOE_ERR_NULL
+    assert call(sync=0x7f0000200040) == moe.MOE_ERR_ALIGN
+    assert call(sync_bytes=1024) == moe.MOE_ERR_WORKSPACE
+    assert call(ws_bytes=1024) == moe.MOE_ERR_WORKSPACE
+    assert call(w=bf) == moe.MOE_ERR_UNSUPPORTED   # bf16 weights
+    assert "one-launch" in moe.moe_last_error()
+    assert call(bm=32) == moe.MOE_ERR_UNSUPPORTED  # 16-row blocks only
+    assert call(M=65) == moe.MOE_ERR_UNSUPPORTED   # decode batches only
+    assert call(M=0, sync=0) == moe.MOE_OK        # empty batch: no-op
