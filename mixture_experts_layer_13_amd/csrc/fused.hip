@@ -10,7 +10,8 @@
 // discrete kernels cost mostly their own dispatch and ramp, so this launch
 // runs them as phases of one persistent grid:
 //
-//   A  max |x| over a grid-stride share of x   -> barrier 0 (max reduced)
+//   A  max |x| over a grid-stride share of x   -> barrier 0 (max reduced);
+//      up to kSmallX values every workgroup reduces all of x, no barrier
 //   B  E4M3 codes of x, s_x = fl32(amax / 448)  -> barrier 1
 //   C  gate/up on the weight ring (ring.hpp), h in fp32, each workgroup's
 //      max |h|                                  -> barrier 2 (max reduced)
@@ -33,8 +34,8 @@
 // after kSpinLimit polls a workgroup records the barrier in the error word
 // and goes on (its results are then wrong, but every wave ends).  Release
 // words and maxima carry the call's epoch (one more than the last call's),
-// so neither needs a reset; the epoch word advances when barrier 0 or 1
-// (whichever is the call's first) completes, when every workgroup has read it.
+// so neither needs a reset; the epoch word advances when the call's first
+// barrier (0 or 1) completes, when every workgroup has read it.
 //
 // Hand-offs between phases: every value one workgroup writes for another is
 // stored device-coherent (sc1) before the writer arrives at the next barrier
@@ -61,15 +62,16 @@ constexpr int kMaxRb = 65536 / 32;
 constexpr size_t kFusedSyncBytes = (size_t)(kWRb + kMaxRb) * 4;
 constexpr int kFusedWpc = 2;
 constexpr int kSlotBytes = 64;
+constexpr size_t kSmallX = 32768;  // values of x every workgroup reduces itself
 
 static_assert(kFusedSyncBytes <= 32768, "sync buffer");
 static_assert(kWErr * 4 == 128, "error word offset");
 
-// Synchronisation words are read and written with atomic read-modify-write
-// operations only: those are performed at the device-coherent level, while a
-// plain or device-scope load of a word this XCD's L2 already holds may be
-// served from that line (measured: a release word polled with device-scope
-// loads never changed for workgroups on other XCDs).
+// Synchronisation words are written with atomic read-modify-writes, which
+// are performed at the device-coherent level, and read with device-scope
+// operations (the compiler turns the idempotent or-0 of rmw_read into a
+// device-scope load); every XCD has its own L2, and a plain load could be
+// served from a line that L2 holds.
 __device__ __forceinline__ uint32_t rmw_read(uint32_t* p) {
   return __hip_atomic_fetch_or(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -79,8 +81,12 @@ __device__ __forceinline__ void rmw_write(uint32_t* p, uint32_t v) {
 
 // Grid barrier b (all threads of the workgroup call it).  payload >= 0: this
 // workgroup's contribution to the barrier's maximum, returned reduced over
-// the grid.  first: the call's first barrier (advances the epoch).  Each
-// group polls its own copy of the release word.
+// the grid (contributions of 0 are skipped: a maximum whose tag is not this
+// call's epoch reads as 0).  first: the call's first barrier (advances the
+// epoch).  The maximum is raised on the group's word (next to its counter)
+// and the group's last arrival folds it into the barrier's word, so that no
+// more than one group's atomics queue on one address.  Each group polls its
+// own copy of the release word.
 __device__ float grid_barrier(uint32_t* sync, int b, uint32_t epoch, float payload, bool first,
                               float* bcast) {
   // the stores of every wave have completed (device-coherent ones at the
@@ -93,18 +99,27 @@ __device__ float grid_barrier(uint32_t* sync, int b, uint32_t epoch, float paylo
     unsigned long long* mx = reinterpret_cast<unsigned long long*>(top + kLineWords);
     uint32_t* rel = top + 2 * kLineWords;  // kBarGroups copies, one line each
     const unsigned long long tag = (unsigned long long)epoch << 32;
-    if (payload >= 0.0f)
-      (void)__hip_atomic_fetch_max(mx, tag | __float_as_uint(payload), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-    wait_vmcnt<0>();
     const int G = gridDim.x;
     const int grp = blockIdx.x % kBarGroups;
     const int ngroups = G < kBarGroups ? G : kBarGroups;
     const uint32_t members = (uint32_t)(G / kBarGroups + (grp < G % kBarGroups ? 1 : 0));
     uint32_t* gc = bar + grp * kLineWords;
+    unsigned long long* gmx = reinterpret_cast<unsigned long long*>(gc + 2);
+    if (payload > 0.0f) {
+      (void)__hip_atomic_fetch_max(gmx, tag | __float_as_uint(payload), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+      wait_vmcnt<0>();
+    }
     const uint32_t old = __hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == members - 1u) {
       rmw_write(gc, 0u);
+      if (payload >= 0.0f) {
+        const unsigned long long m =
+            __hip_atomic_fetch_or(gmx, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((m >> 32) == epoch && (uint32_t)m != 0u)
+          (void)__hip_atomic_fetch_max(mx, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wait_vmcnt<0>();
+      }
       const uint32_t o2 = __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (o2 == (uint32_t)ngroups - 1u) {
         rmw_write(top, 0u);
@@ -227,18 +242,23 @@ void fused_decode_kernel(
   // ---- A: s_x
   const size_t nx = (size_t)a.M * a.K;  // a multiple of 8
   float sx;
+  const bool small_x = nx <= kSmallX;
   if (a1_scale) {
     sx = *a1_scale;
   } else {
+    // small x: every workgroup reduces all of it (from L2 after the first
+    // touch) and no barrier is needed; else a grid-stride share each
+    const size_t i0 = small_x ? (size_t)tid * 8 : gtid * 8;
+    const size_t step = small_x ? (size_t)kRingThreads * 8 : gthreads * 8;
     float m = 0.0f;
-    for (size_t i = gtid * 8; i < nx; i += gthreads * 8) {
+    for (size_t i = i0; i < nx; i += step) {
       float v[8];
       fused_load8<XT>(a.x, i, v);
 #pragma unroll
       for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
     }
     m = block_max_ring(m, red);
-    const float amax = grid_barrier(sync, 0, epoch, m, true, &bcast);
+    const float amax = small_x ? m : grid_barrier(sync, 0, epoch, m, true, &bcast);
     sx = (amax == 0.0f) ? 1.0f : amax / 448.0f;
   }
 
@@ -251,7 +271,7 @@ void fused_decode_kernel(
       coh_st8(xr, (uint32_t)i, codes8(v, sx));
     }
   }
-  grid_barrier(sync, 1, epoch, -1.0f, a1_scale != nullptr, &bcast);
+  grid_barrier(sync, 1, epoch, -1.0f, a1_scale != nullptr || small_x, &bcast);
 
   // ---- C: gate/up
   GemmArgs g1 = a;
