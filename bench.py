@@ -276,8 +276,7 @@ def rope_main(args):
     achieved = alg / (med * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "rope_amax_kernel + rope_quant_kernel (one rope_one_kernel for small batches)" if n > (1 << 18)
-            else "rope_one_kernel",
+            "kernel": "rope_amax_kernel + rope_quant_kernel" if n > (1 << 15) else "rope_one_kernel",
             "avg_launch_us": round(float(us.mean()), 2), "algorithmic_bytes_per_launch": int(alg)}
     cpu = None
     if args.cpu_sample > 0:
