@@ -16,8 +16,8 @@
 //   C  gate/up on the weight ring (ring.hpp), h in fp32, each workgroup's
 //      max |h|                                  -> barrier 2 (max reduced)
 //   D  E4M3 codes of h, s_h = fl32(hmax / 448)  -> barrier 3
-//   E  down on the weight ring; the workgroup that finishes the last column
-//      group of a 32-row output block sums that block over the top-k slots.
+//   E  down on the weight ring, y per pair              -> barrier 4
+//   F  the weighted top-k combine, every thread one group of 8 outputs.
 //
 // Every phase computes what the discrete kernels compute, in the same
 // arithmetic, so the output equals moe_fused_forward's wherever both run the
@@ -48,18 +48,16 @@ namespace moe {
 
 constexpr int kLineWords = 32;  // 128-byte line
 constexpr int kBarGroups = 16;
-constexpr int kFusedBarriers = 4;
+constexpr int kFusedBarriers = 5;
 constexpr int kSpinLimit = 1 << 20;
 // sync words: epoch, error, then per barrier kBarGroups group counters, the
 // top counter, the 64-bit maximum and kBarGroups copies of the release word
-// (each in its own line), then the [K / 32] output-block counters
+// (each in its own line)
 constexpr int kWEpoch = 0;
 constexpr int kWErr = kLineWords;
 constexpr int kWBar = 2 * kLineWords;
 constexpr int kBarLines = 2 * kBarGroups + 2;  // groups, top, max, release copies
-constexpr int kWRb = kWBar + kFusedBarriers * kBarLines * kLineWords;
-constexpr int kMaxRb = 65536 / 32;
-constexpr size_t kFusedSyncBytes = (size_t)(kWRb + kMaxRb) * 4;
+constexpr size_t kFusedSyncBytes = (size_t)(kWBar + kFusedBarriers * kBarLines * kLineWords) * 4;
 constexpr int kFusedWpc = 2;
 constexpr int kSlotBytes = 64;
 constexpr size_t kSmallX = 32768;  // values of x every workgroup reduces itself
@@ -192,6 +190,68 @@ __device__ __forceinline__ float block_max_ring(float v, float* red) {
   return r;
 }
 
+template <int OT>
+__device__ __forceinline__ void fused_combine(const GemmArgs& a, size_t gtid, size_t gthreads) {
+  const auto yr = dev_rsrc(a.y);
+  constexpr int ES = OT == DT_BF16 ? 2 : 4;
+  const size_t rows = (size_t)(*a.num_padded);
+  const int groups = a.K / 8;
+  const size_t items = (size_t)a.M * groups;
+  for (size_t it = gtid; it < items; it += gthreads) {
+    const int t = (int)(it / groups), n = (int)(it - (size_t)t * groups) * 8;
+    const int rb = n >> 5, c = n & 31;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    for (int j0 = 0; j0 < a.topk; j0 += 8) {
+      int pos[8];
+      float w[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool ok = j0 + j < a.topk;
+        pos[j] = ok ? a.pair_pos[(size_t)t * a.topk + j0 + j] : -1;
+        w[j] = ok ? a.topk_w[(size_t)t * a.topk + j0 + j] : 0.0f;
+      }
+      i32x4 q[8][2];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t at =
+            (uint32_t)((((size_t)rb * rows + (pos[j] < 0 ? 0 : pos[j])) * 32 + c) * ES);
+#pragma unroll
+        for (int u = 0; u < (OT == DT_BF16 ? 1 : 2); ++u)
+          q[j][u] = pos[j] >= 0 ? coh_ld16(yr, at + 16 * u) : i32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (pos[j] < 0) continue;
+        if (OT == DT_BF16) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[2 * i] += w[j] * bf16_bits_to_f32((uint32_t)q[j][0][i] & 0xffffu);
+            v[2 * i + 1] += w[j] * bf16_bits_to_f32((uint32_t)q[j][0][i] >> 16);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[i] += w[j] * __int_as_float(q[j][0][i]);
+            v[4 + i] += w[j] * __int_as_float(q[j][1][i]);
+          }
+        }
+      }
+    }
+    const size_t o = (size_t)t * a.K + n;
+    if (OT == DT_BF16) {
+      uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + o;
+      *reinterpret_cast<uint2*>(out) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      *reinterpret_cast<uint2*>(out + 4) = make_uint2(pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    } else {
+      float* out = reinterpret_cast<float*>(a.out) + o;
+      st16(out, i32x4{__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3])});
+      st16(out + 4, i32x4{__float_as_int(v[4]), __float_as_int(v[5]), __float_as_int(v[6]), __float_as_int(v[7])});
+    }
+  }
+}
+
 // One ring phase as ring_gemm_kernel<E4M3, 0, D, ...> runs it: column groups
 // of two 16-row blocks where that removes an eighth of the groups.
 template <bool G1>
@@ -277,7 +337,7 @@ void fused_decode_kernel(
   GemmArgs g1 = a;
   g1.x = xq;
   g1.xt = DT_E4M3;
-  fused_ring<true>(g1, GT1, lds, RingFused{sx, &hmax_slot, nullptr});
+  fused_ring<true>(g1, GT1, lds, RingFused{sx, &hmax_slot});
 
   // ---- s_h
   float sh;
@@ -289,13 +349,15 @@ void fused_decode_kernel(
     sh = (hm == 0.0f) ? 1.0f : hm / 448.0f;
   }
 
-  // ---- D: codes of h ([num_padded, N] fp32, read device-coherent)
+  // ---- D: codes of h ([num_padded, N] fp32, read device-coherent; the
+  // padding rows' codes are never used: their columns' sums are dropped)
   {
     const size_t rows = (size_t)(*a.num_padded), nh = rows * a.N;
     const auto hr = dev_rsrc(a.h);
     const auto qr = dev_rsrc(a.hq);
     for (size_t i = gtid * 8; i < nh; i += gthreads * 8) {
       const size_t r = i / a.N, n = i - r * a.N;  // 8 columns of one 16-column block
+      if (a.sorted_ids[r] >= a.P) continue;
       const uint32_t at = (uint32_t)((((n >> 4) * rows + r) * 16 + (n & 15)) * 4);
       const i32x4 p = coh_ld16(hr, at), q = coh_ld16(hr, at + 16);
       float v[8];
@@ -310,7 +372,16 @@ void fused_decode_kernel(
   grid_barrier(sync, 3, epoch, -1.0f, false, &bcast);
 
   // ---- E: down and the combine
-  fused_ring<false>(a, GT2, lds, RingFused{sh, nullptr, sync + kWRb});
+  fused_ring<false>(a, GT2, lds, RingFused{sh, nullptr});
+  grid_barrier(sync, 4, epoch, -1.0f, false, &bcast);
+
+  // ---- F: out[t, n .. n + 7] = sum over the slots, in slot order, of
+  // w[t, j] * y[pair_pos[t, j]] (the combine kernel's arithmetic), y read
+  // device-coherent from its tiled layout [K / 32][rows][32]
+  if (a.ot == DT_BF16)
+    fused_combine<DT_BF16>(a, gtid, gthreads);
+  else
+    fused_combine<DT_F32>(a, gtid, gthreads);
 
   if (blockIdx.x == 0 && tid == 0) {
     const_cast<float*>(a.sx)[0] = sx;
@@ -337,7 +408,7 @@ bool fused_decode_applies(const GemmArgs& a) {
   if (a.wt != DT_E4M3 || !(a.xt == DT_BF16 || a.xt == DT_F32)) return false;
   if (!(a.ot == DT_BF16 || a.ot == DT_F32)) return false;
   if (a.M < 1 || a.M > kStreamMaxM || a.block_m != 16) return false;
-  if (a.N % 16 || a.K % 32 || a.K / 32 > kMaxRb) return false;
+  if (a.N % 16 || a.K % 32) return false;
   GemmArgs r = a;
   r.xt = DT_E4M3;
   if (!ring_rows(r, a.K) || !ring_rows(r, a.N) || !ring_pair_fits(r)) return false;

@@ -299,81 +299,14 @@ __device__ __forceinline__ i32x4 coh_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off
 // What the single-launch forward (fused.hip) changes in ring_run: the scale
 // of the activation operand comes in as a value (it was reduced over the
 // grid inside the launch), the gate/up epilogue leaves its max |h| in LDS
-// instead of raising a global maximum, h and y are stored device-coherent
-// in tiled layouts that give every 128-byte line one writer (h [N / 16]
-// [rows][16], y [K / 32][rows][32], rows = the padded pair count),
-// and every finished down task counts itself on its 32-row block of the
-// output; the workgroup that completes a block's count sums it over the
-// top-k slots (the weighted combine) and resets the count for the next call.
+// instead of raising a global maximum, and h and y are stored
+// device-coherent in tiled layouts that give every 128-byte line one writer
+// (h [N / 16][rows][16], y [K / 32][rows][32], rows = the padded pair
+// count).
 struct RingFused {
-  float act_scale;       // s_x (gate/up) or s_h (down)
-  float* hmax;           // LDS slot of the gate/up epilogue wave's max |h|
-  uint32_t* rb_count;    // [K / 32] finished column groups per output block
+  float act_scale;  // s_x (gate/up) or s_h (down)
+  float* hmax;      // LDS slot of the gate/up epilogue wave's max |h|
 };
-
-// out[t, 32 rb .. 32 rb + 31] for every token t: the sum over the top-k
-// slots, in slot order, of w[t, j] * y[pair_pos[t * k + j]] in fp32 (the
-// arithmetic of combine_kernel), y read device-coherent from its tiled
-// layout [K / 32][rows][32].  One wave; a lane
-// takes 8 consecutive outputs of one token.
-template <int OT>
-__device__ __forceinline__ void fused_combine_block(const GemmArgs& a, int rb, int lane) {
-  const auto yr = dev_rsrc(a.y);
-  constexpr int ES = OT == DT_BF16 ? 2 : 4;
-  const size_t rows = (size_t)(*a.num_padded);  // y tiled [K / 32][rows][32]
-  for (int it = lane; it < a.M * 4; it += kWave) {
-    const int t = it >> 2, n = 32 * rb + 8 * (it & 3);
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-    for (int j0 = 0; j0 < a.topk; j0 += 8) {
-      int pos[8];
-      float w[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool ok = j0 + j < a.topk;
-        pos[j] = ok ? a.pair_pos[(size_t)t * a.topk + j0 + j] : -1;
-        w[j] = ok ? a.topk_w[(size_t)t * a.topk + j0 + j] : 0.0f;
-      }
-      i32x4 q[8][2];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t at =
-            (uint32_t)((((size_t)rb * rows + (pos[j] < 0 ? 0 : pos[j])) * 32 + (n - 32 * rb)) * ES);
-#pragma unroll
-        for (int u = 0; u < (OT == DT_BF16 ? 1 : 2); ++u)
-          q[j][u] = pos[j] >= 0 ? coh_ld16(yr, at + 16 * u) : i32x4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (pos[j] < 0) continue;
-        if (OT == DT_BF16) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            v[2 * i] += w[j] * bf16_bits_to_f32((uint32_t)q[j][0][i] & 0xffffu);
-            v[2 * i + 1] += w[j] * bf16_bits_to_f32((uint32_t)q[j][0][i] >> 16);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            v[i] += w[j] * __int_as_float(q[j][0][i]);
-            v[4 + i] += w[j] * __int_as_float(q[j][1][i]);
-          }
-        }
-      }
-    }
-    const size_t o = (size_t)t * a.K + n;
-    if (OT == DT_BF16) {
-      uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + o;
-      *reinterpret_cast<uint2*>(out) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      *reinterpret_cast<uint2*>(out + 4) = make_uint2(pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
-    } else {
-      float* out = reinterpret_cast<float*>(a.out) + o;
-      st16(out, i32x4{__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3])});
-      st16(out + 4, i32x4{__float_as_int(v[4]), __float_as_int(v[5]), __float_as_int(v[6]), __float_as_int(v[7])});
-    }
-  }
-}
 
 // Workgroup = kRingWaves streaming waves (each one K-step of every stage) and
 // one epilogue wave.  The epilogue wave sums the streaming waves' partial
@@ -553,21 +486,6 @@ __device__ __forceinline__ void ring_run(const GemmArgs& a, int GT, char* lds, c
             st16(y + o + 16, i32x4{__float_as_int(v1[0]), __float_as_int(v1[1]),
                                    __float_as_int(v1[2]), __float_as_int(v1[3])});
           }
-        }
-      }
-      if constexpr (FUSED && !G1) {
-        // this task's rows of y have reached the device-coherent level; the
-        // column group that completes block rb's count combines it
-        wait_vmcnt<0>();
-        uint32_t old = 0;
-        if (lane == 0) old = __hip_atomic_fetch_add(fz.rb_count + rb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        old = __shfl(old, 0, kWave);
-        if (old == (uint32_t)ngrp - 1u) {
-          if (lane == 0) __hip_atomic_store(fz.rb_count + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (a.ot == DT_BF16)
-            fused_combine_block<DT_BF16>(a, rb, lane);
-          else
-            fused_combine_block<DT_F32>(a, rb, lane);
         }
       }
     }
