@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--head-dim", type=int, default=128)
     ap.add_argument("--persistent", action="store_true",
                     help="E4M3 decode: run the forward as one launch (moe_fused_forward_persistent)")
+    ap.add_argument("--in-kernel-x", action="store_true",
+                    help="with --persistent: quantise x inside the one launch instead of beside the routing")
     ap.add_argument("--copy-check", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -341,7 +343,7 @@ def main():
     H, I, E, k = d["H"], d["I"], d["E"], d["topk"]
     layer = moe.FusedMoE(T, H, I, E, k, d["w13"], d["w2"], d["w13_scale"], d["w2_scale"],
                          a_dtype=wl.x_dtype, out_dtype=wl.out_dtype, device=dev,
-                         persistent=args.persistent)
+                         persistent=args.persistent, prequant=not args.in_kernel_x)
     x, logits = d["x"], d["logits"]
 
     ev = HipEvents()
@@ -365,6 +367,8 @@ def main():
         ev.record(sev[2 * i], st.cuda_stream)
         if args.persistent:  # the one launch of the forward between the kernel events
             layer.route(logits)
+            if layer.prequant:
+                layer.quantize(x)
             ev.record(kev[4 * i], st.cuda_stream)
             layer.forward(x)
             ev.record(kev[4 * i + 1], st.cuda_stream)
@@ -445,8 +449,12 @@ def main():
 
     if args.persistent:
         # the dominant (only) kernel is the whole forward: its bytes are the
-        # op's, less the routing's logits and ids, which the routing launch reads
+        # op's, less the routing's logits and ids, which the routing launch
+        # reads (and, when x is quantised beside the routing, x itself: the
+        # launch then reads its codes)
         g1_bytes = op_bytes - T * E * 4 - T * k * 8
+        if layer.prequant:
+            g1_bytes += T * H * (1 - bx)
     if hbm_bound:
         achieved = g1_bytes / (g1_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -470,6 +478,8 @@ def main():
     roof["algorithmic_bytes_per_launch"] = int(g1_bytes)
     src_sha = kernel_source_sha()
     key = f"{args.workload}:T{T}" + (":persistent" if args.persistent else "")
+    if args.persistent:
+        roof["x_quantised"] = "inside the launch" if args.in_kernel_x else "beside the routing (moe_quantize_act)"
     if os.path.exists(PMC_FILE):
         rec = json.load(open(PMC_FILE)).get(key)
         if rec and rec.get("gemm_source_sha256") == src_sha:

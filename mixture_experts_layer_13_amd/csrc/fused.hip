@@ -10,6 +10,8 @@
 // discrete kernels cost mostly their own dispatch and ramp, so this launch
 // runs them as phases of one persistent grid:
 //
+// (pre-quantised activations, the codes and their scale from
+// moe_quantize_act, start at C)
 //   A  max |x| over a grid-stride share of x   -> barrier 0 (max reduced);
 //      up to kSmallX values every workgroup reduces all of x, no barrier
 //   B  E4M3 codes of x, s_x = fl32(amax / 448)  -> barrier 1
@@ -299,53 +301,60 @@ void fused_decode_kernel(
   __syncthreads();
   const uint32_t epoch = epoch_slot;
 
-  // ---- A: s_x
-  const size_t nx = (size_t)a.M * a.K;  // a multiple of 8
-  float sx;
-  const bool small_x = nx <= kSmallX;
-  if (a1_scale) {
+  // pre-quantised activations (XT = E4M3: the codes with their scale in
+  // a1_scale) skip phases A and B
+  constexpr bool pre = XT == DT_E4M3;
+  float sx = 1.0f;
+  if constexpr (pre) {
     sx = *a1_scale;
   } else {
-    // small x: every workgroup reduces all of it (from L2 after the first
-    // touch) and no barrier is needed; else a grid-stride share each
-    const size_t i0 = small_x ? (size_t)tid * 8 : gtid * 8;
-    const size_t step = small_x ? (size_t)kRingThreads * 8 : gthreads * 8;
-    float m = 0.0f;
-    for (size_t i = i0; i < nx; i += step) {
-      float v[8];
-      fused_load8<XT>(a.x, i, v);
+    // ---- A: s_x
+    const size_t nx = (size_t)a.M * a.K;  // a multiple of 8
+    const bool small_x = nx <= kSmallX;
+    if (a1_scale) {
+      sx = *a1_scale;
+    } else {
+      // small x: every workgroup reduces all of it (from L2 after the first
+      // touch) and no barrier is needed; else a grid-stride share each
+      const size_t i0 = small_x ? (size_t)tid * 8 : gtid * 8;
+      const size_t step = small_x ? (size_t)kRingThreads * 8 : gthreads * 8;
+      float m = 0.0f;
+      for (size_t i = i0; i < nx; i += step) {
+        float v[8];
+        fused_load8<XT>(a.x, i, v);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
+      }
+      m = block_max_ring(m, red);
+      const float amax = small_x ? m : grid_barrier(sync, 0, epoch, m, true, &bcast);
+      sx = (amax == 0.0f) ? 1.0f : amax / 448.0f;
     }
-    m = block_max_ring(m, red);
-    const float amax = small_x ? m : grid_barrier(sync, 0, epoch, m, true, &bcast);
-    sx = (amax == 0.0f) ? 1.0f : amax / 448.0f;
-  }
 
-  // ---- B: codes of x
-  {
-    const auto xr = dev_rsrc(xq);
-    for (size_t i = gtid * 8; i < nx; i += gthreads * 8) {
-      float v[8];
-      fused_load8<XT>(a.x, i, v);
-      coh_st8(xr, (uint32_t)i, codes8(v, sx));
+    // ---- B: codes of x
+    {
+      const auto xr = dev_rsrc(xq);
+      for (size_t i = gtid * 8; i < nx; i += gthreads * 8) {
+        float v[8];
+        fused_load8<XT>(a.x, i, v);
+        coh_st8(xr, (uint32_t)i, codes8(v, sx));
+      }
     }
+    grid_barrier(sync, 1, epoch, -1.0f, a1_scale != nullptr || small_x, &bcast);
   }
-  grid_barrier(sync, 1, epoch, -1.0f, a1_scale != nullptr || small_x, &bcast);
 
   // ---- C: gate/up
   GemmArgs g1 = a;
-  g1.x = xq;
+  g1.x = pre ? a.x : xq;
   g1.xt = DT_E4M3;
   fused_ring<true>(g1, GT1, lds, RingFused{sx, &hmax_slot});
 
   // ---- s_h
   float sh;
   if (a2_scale) {
-    grid_barrier(sync, 2, epoch, -1.0f, false, &bcast);
+    grid_barrier(sync, 2, epoch, -1.0f, pre, &bcast);
     sh = *a2_scale;
   } else {
-    const float hm = grid_barrier(sync, 2, epoch, hmax_slot, false, &bcast);
+    const float hm = grid_barrier(sync, 2, epoch, hmax_slot, pre, &bcast);
     sh = (hm == 0.0f) ? 1.0f : hm / 448.0f;
   }
 
@@ -401,11 +410,11 @@ static size_t fused_lds(const GemmArgs& a) {
 }
 
 // The launch shape fused_decode_kernel assumes: E4M3 weights, x in bf16 or
-// fp32, 16-row alignment blocks whose pairing scan covers E, rows of whole
+// fp32 or already E4M3 codes, 16-row alignment blocks whose pairing scan covers E, rows of whole
 // ring stages, every 32-bit byte offset in range, and LDS for two
 // workgroups per CU.
 bool fused_decode_applies(const GemmArgs& a) {
-  if (a.wt != DT_E4M3 || !(a.xt == DT_BF16 || a.xt == DT_F32)) return false;
+  if (a.wt != DT_E4M3 || !(a.xt == DT_BF16 || a.xt == DT_F32 || a.xt == DT_E4M3)) return false;
   if (!(a.ot == DT_BF16 || a.ot == DT_F32)) return false;
   if (a.M < 1 || a.M > kStreamMaxM || a.block_m != 16) return false;
   if (a.N % 16 || a.K % 32) return false;
@@ -439,13 +448,17 @@ static int fused_setup() {
 
 int launch_fused_decode(const GemmArgs& a, uint8_t* xq, uint32_t* sync, const float* a1_scale,
                         const float* a2_scale, hipStream_t st) {
-  const int err = a.xt == DT_BF16 ? fused_setup<DT_BF16>() : fused_setup<DT_F32>();
+  const int err = a.xt == DT_BF16 ? fused_setup<DT_BF16>()
+                  : a.xt == DT_F32 ? fused_setup<DT_F32>() : fused_setup<DT_E4M3>();
   if (err) return err;
   const dim3 grid(kFusedWpc * device_cu_count());
   const size_t lds = fused_lds(a);
   const int gt1 = FusedG1::table_rows(a), gt2 = FusedG2::table_rows(a);
   if (a.xt == DT_BF16)
     hipLaunchKernelGGL(fused_decode_kernel<DT_BF16>, grid, dim3(kRingThreads), lds, st, a, xq, sync,
+                       gt1, gt2, a1_scale, a2_scale);
+  else if (a.xt == DT_E4M3)
+    hipLaunchKernelGGL(fused_decode_kernel<DT_E4M3>, grid, dim3(kRingThreads), lds, st, a, xq, sync,
                        gt1, gt2, a1_scale, a2_scale);
   else
     hipLaunchKernelGGL(fused_decode_kernel<DT_F32>, grid, dim3(kRingThreads), lds, st, a, xq, sync,

@@ -102,8 +102,8 @@ moe_status check_problem(const moe_problem* p) {
     return fail(MOE_ERR_SHAPE, "block_m=%d must be 16, 32, 64, 128 or 256", p->block_m);
   for (int dt : {p->a_dtype, p->w_dtype, p->out_dtype})
     if (dt < MOE_F32 || dt > MOE_FP8_E4M3) return fail(MOE_ERR_DTYPE, "unknown dtype code %d", dt);
-  if (p->a_dtype == MOE_FP8_E4M3)
-    return fail(MOE_ERR_UNSUPPORTED, "activations must be f32 or bf16 (FP8 quantisation is internal)");
+  if (p->a_dtype == MOE_FP8_E4M3 && p->w_dtype != MOE_FP8_E4M3)
+    return fail(MOE_ERR_UNSUPPORTED, "E4M3 activations need E4M3 weights");
   if (p->out_dtype == MOE_FP8_E4M3) return fail(MOE_ERR_UNSUPPORTED, "output must be f32 or bf16");
   long long cap = moe_align_capacity(p->M, p->topk, p->E, p->block_m);
   if ((long long)cap * p->K > (1LL << 40))
@@ -287,8 +287,14 @@ moe_status fused_forward(const moe_problem* p, const void* a, const void* w13, c
   moe_status s = check_problem(p);
   if (s) return s;
   if (p->M == 0) return ok();
+  if (p->a_dtype == MOE_FP8_E4M3 && !persistent)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "activations must be f32 or bf16 (FP8 quantisation is internal; pre-quantised "
+                "codes only in moe_fused_forward_persistent)");
   if (persistent) {
     if (!sync) return fail(MOE_ERR_NULL, "sync is NULL");
+    if (p->a_dtype == MOE_FP8_E4M3 && !a1_scale)
+      return fail(MOE_ERR_NULL, "E4M3 activations need their scale in a1_scale");
     if (!aligned(sync, 128)) return fail(MOE_ERR_ALIGN, "sync must be 128-byte aligned");
     if (sync_bytes < MOE_FUSED_SYNC_BYTES)
       return fail(MOE_ERR_WORKSPACE, "sync buffer of %d bytes needed, %zu given",

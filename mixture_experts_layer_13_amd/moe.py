@@ -333,7 +333,7 @@ class FusedMoE:
     def __init__(self, M, K, N, E, topk, w13, w2, w13_scale=None, w2_scale=None,
                  block_m=None, a_dtype=torch.bfloat16, out_dtype=torch.bfloat16,
                  renormalize=True, a1_scale=None, a2_scale=None, device="cuda",
-                 persistent=False):
+                 persistent=False, prequant=True):
         if block_m is None:
             # alignment block: 16 rows for decode-sized batches (the stream and
             # ring kernels), 256 once the experts average 512 rows or more (the
@@ -350,9 +350,18 @@ class FusedMoE:
         self.topk_weights = torch.empty(M, topk, dtype=torch.float32, device=device)
         self.alignment = alloc_alignment(M, topk, E, block_m, device)
         self.out = torch.empty(M, K, dtype=out_dtype, device=device)
-        # persistent: the forward runs as one launch (moe_fused_forward_persistent)
+        # persistent: the forward runs as one launch (moe_fused_forward_persistent);
+        # prequant: the activation codes are made first (moe_quantize_act,
+        # next to the routing), and the one launch starts at gate/up
         self.persistent = persistent
         self.sync = alloc_fused_sync(device) if persistent else None
+        self.prequant = persistent and prequant and w13.dtype == torch.float8_e4m3fn
+        if self.prequant:
+            self.problem_q = make_problem(M, K, N, E, topk, block_m, torch.float8_e4m3fn,
+                                          w13.dtype, out_dtype)
+            self.xq = torch.empty(M, K, dtype=torch.uint8, device=device)
+            self.xscale = torch.empty(1, dtype=torch.float32, device=device)
+            self.qws = torch.empty(MOE_QUANT_WORKSPACE_BYTES, dtype=torch.uint8, device=device)
 
     def act_scales(self):
         """Device view of the (s_x, s_h) fp32 pair that the last E4M3 forward
@@ -362,14 +371,25 @@ class FusedMoE:
 
     def __call__(self, x, logits, stream=None, events=None):
         self.route(logits, stream)
+        if self.prequant:
+            self.quantize(x, stream)
         return self.forward(x, stream, events)
 
     def route(self, logits, stream=None):
         moe_route_align(logits, self.topk, self.renormalize, self.block_m, self.workspace,
                         self.topk_ids, self.topk_weights, self.alignment, stream)
 
+    def quantize(self, x, stream=None):
+        """The activation codes and scale of x (prequant mode)."""
+        moe_quantize_act(x, self.a1_scale, self.xq, self.xscale, self.qws, stream)
+
     def forward(self, x, stream=None, events=None):
-        if self.persistent:
+        if self.prequant:
+            moe_fused_forward_persistent(self.problem_q, self.xq, self.w13, self.w2,
+                                         self.topk_weights, self.alignment, self.out,
+                                         self.workspace, self.sync, self.w13_scale,
+                                         self.w2_scale, self.xscale, self.a2_scale, stream)
+        elif self.persistent:
             moe_fused_forward_persistent(self.problem, x, self.w13, self.w2, self.topk_weights,
                                          self.alignment, self.out, self.workspace, self.sync,
                                          self.w13_scale, self.w2_scale, self.a1_scale,

@@ -311,3 +311,6 @@ def test_persistent_forward_rejects_without_launch():
     assert call(bm=32) == moe.MOE_ERR_UNSUPPORTED  # 16-row blocks only
     assert call(M=65) == moe.MOE_ERR_UNSUPPORTED   # decode batches only
     assert call(M=0, sync=0) == moe.MOE_OK        # empty batch: no-op
+    # pre-quantised activations: only with E4M3 weights, only here, and with their scale
+    assert call(a=e4) == moe.MOE_ERR_NULL and "a1_scale" in moe.moe_last_error()
+    assert call(a=e4, w=bf) == moe.MOE_ERR_UNSUPPORTED

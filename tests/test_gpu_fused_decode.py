@@ -204,3 +204,26 @@ def test_persistent_graph_replay():
         assert torch.equal(fz.out, eager), r
         assert _check_sync(fz.sync, f"replay {r}") == e0 + r + 1
     del g
+
+
+@pytest.mark.parametrize("T,xdt", [(1, torch.bfloat16), (33, torch.bfloat16), (64, torch.float32)])
+def test_persistent_in_kernel_x_equals_prequantised(T, xdt):
+    """The two ways of making the activation codes for the one launch: inside
+    it (phases A and B, grid barriers 0 and 1) or beside the routing with
+    moe_quantize_act, the launch then taking E4M3 codes and their scale.
+    Same codes, same scale, so the outputs are equal bit for bit."""
+    w = inputs.WORKLOADS["decode_fp8"]
+    d = inputs.make_inputs(w, T, device=DEV, seed=900 + T)
+    d["x"] = d["x"].to(xdt)
+    outs = []
+    for pre in (False, True):
+        layer = moe.FusedMoE(T, w.H, w.I, w.E, w.topk, d["w13"], d["w2"], d["w13_scale"],
+                             d["w2_scale"], block_m=16, a_dtype=xdt, out_dtype=w.out_dtype,
+                             device=DEV, persistent=True, prequant=pre)
+        assert layer.prequant == pre
+        outs.append((layer(d["x"], d["logits"]).clone(), layer.act_scales().clone()))
+        torch.cuda.synchronize()
+        _check_sync(layer.sync, f"T={T} {xdt} prequant={pre}")
+    assert torch.equal(outs[0][1], outs[1][1])
+    assert torch.equal(outs[0][0], outs[1][0])
+
