@@ -27,7 +27,7 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 2500.0, "e4m3": 5000.0}
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 MFMA_FILE = os.path.join(ROOT, "profiles", "pmc_mfma.json")
 KERNEL_SRCS = [os.path.join(ROOT, "mixture_experts_layer_13_amd", "csrc", f)
-               for f in ("gemm.hip", "ring.hip", "prefill.hip", "prefill2.hip", "common.hpp")]
+               for f in ("gemm.hip", "ring.hip", "ring.hpp", "prefill.hip", "prefill2.hip", "common.hpp")]
 
 
 def kernel_source_sha():
