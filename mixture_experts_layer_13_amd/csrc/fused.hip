@@ -258,6 +258,11 @@ __device__ __forceinline__ void fused_combine(const GemmArgs& a, size_t gtid, si
 // of two 16-row blocks where that removes an eighth of the groups.
 template <bool G1>
 __device__ __forceinline__ void fused_ring(const GemmArgs& a, int GT, char* lds, RingFused fz) {
+  if (a.P <= 16) {  // no expert holds two blocks: no pairing scan
+    ring_run<DT_E4M3, 1, kRingD, G1, true>(a, GT, lds, nullptr, 0, fz);
+    __syncthreads();
+    return;
+  }
   int base;
   const int npair = pair_scan(a, reinterpret_cast<int*>(lds + kRingD * kG1StageBytes), base);
   const int nb = *a.num_padded / a.block_m;

@@ -67,7 +67,8 @@ template <bool G1>
 static int ring_dispatch(const GemmArgs& a, hipStream_t st, bool run) {
   if (a.block_m > 16)
     return a.wt == DT_E4M3 ? ring_try<DT_E4M3, 2, G1>(a, st, run) : ring_try<DT_BF16, 2, G1>(a, st, run);
-  if ((G1 ? kPairG1 : kPairG2) && ring_pair_fits(a))
+  // pairing needs an expert with two 16-row blocks, so more than 16 pairs
+  if ((G1 ? kPairG1 : kPairG2) && a.P > 16 && ring_pair_fits(a))
     return a.wt == DT_E4M3 ? ring_try<DT_E4M3, 0, G1>(a, st, run) : ring_try<DT_BF16, 0, G1>(a, st, run);
   return a.wt == DT_E4M3 ? ring_try<DT_E4M3, 1, G1>(a, st, run) : ring_try<DT_BF16, 1, G1>(a, st, run);
 }
