@@ -143,13 +143,13 @@ __device__ __forceinline__ void q_tile_xv(const GemmArgs& a, QTile<NW>& t, const
   for (int q = 0; q < L::Instr; ++q) {
     const int r = (wv * L::Instr + q) * 8 + (lane >> 3);  // token row of the tile
     const int lc = q_logical(kQRows + r, lane & 7);
-    if (G1) {
-      const int f = ids[r];
-      const int tok = (f >= 0 && f < a.P) ? f / a.topk : 0;  // padding rows read row 0
-      t.xv[q] = (uint32_t)tok * rowb + lc * 16;
-    } else {
-      t.xv[q] = (uint32_t)r * rowb + lc * 16;
-    }
+    // padding rows (past the end of the expert's pairs) take an offset past
+    // every operand buffer (all under 2 GiB): their loads return zeros and
+    // touch no memory, and their products are never stored
+    const int f = ids[r];
+    const bool real = f >= 0 && f < a.P;
+    const uint32_t row = G1 ? (uint32_t)(f / a.topk) * rowb : (uint32_t)r * rowb;
+    t.xv[q] = real ? row + lc * 16 : 0x80000000u;
   }
 }
 
