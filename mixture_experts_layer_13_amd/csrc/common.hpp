@@ -67,6 +67,46 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
   return sign | (e << 3) | ((r >> 20) & 7u);
 }
 
+// Whether e4m3_quotient may use the reciprocal of the scale s.
+__device__ __forceinline__ bool e4m3_fast_scale(float s, float r) {
+  return s >= 1.17549435e-38f && r <= 3.40282347e+38f;
+}
+
+// E4M3(fl32(y / s)) without a division per element: r = fl32(1 / s)
+// correctly rounded, fast = e4m3_fast_scale(s, r) (s a positive normal float
+// with a finite reciprocal; otherwise every quotient is an IEEE division).
+// Markstein's correction step (P. Markstein, IBM J. Res. Dev. 34(1), 1990):
+// q = fl32(y r), the residual e = y - s q from one fused multiply-add (exact),
+// and fl32(q + e r) is the correctly rounded quotient, except possibly within
+// two ulps of a power of two, where the residual can need one bit more than
+// binary32 holds.  Powers of two are E4M3 values, not rounding midpoints --
+// all but 2^-10, the midpoint between 0 and the smallest subnormal 2^-9: a
+// quotient within four ulps of it takes the IEEE division instead.  So the
+// code is that of the correctly rounded quotient in every case.  Quotients
+// beyond 1024 in magnitude keep q (their code saturates whatever the last
+// bits); the sign is y's (so -0 keeps its sign).  The result is clamped to
+// +-448 (a NaN y gives a saturated code, not the NaN code).
+__device__ __forceinline__ float e4m3_quotient(float y, float s, float r, bool fast) {
+  const float q0 = y * r;
+  const float e = __builtin_fmaf(-q0, s, y);
+  float q = __builtin_fmaf(e, r, q0);
+  if (__builtin_fabsf(q0) >= 1024.0f) q = q0;
+  const uint32_t d = (__float_as_uint(q) & 0x7fffffffu) - 0x3a800000u;  // 2^-10
+  if (__builtin_expect(d + 4u <= 8u || !fast, 0)) q = y / s;
+  q = __builtin_copysignf(q, y);
+  return __builtin_fminf(__builtin_fmaxf(q, -448.0f), 448.0f);
+}
+
+// Four E4M3 codes (little-endian) of values already in [-448, 448], by the
+// hardware conversion, which rounds to nearest even like f32_to_e4m3 (checked
+// equal on every E4M3 midpoint, its neighbours and a dense sample of the
+// fp32 range).
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  return (uint32_t)v;
+}
+
 // ----------------------------------------------------------------- memory
 
 __device__ __forceinline__ i32x4 ld16(const void* p) {

@@ -170,14 +170,13 @@ __device__ __forceinline__ void fused_load8(const void* x, size_t i, float v[8])
   }
 }
 
-// Eight codes E4M3(fl32(v / s)) (IEEE division), packed little-endian.
-__device__ __forceinline__ uint2 codes8(const float v[8], float s) {
-  uint32_t lo = 0, hi = 0;
+// Eight codes E4M3(fl32(v / s)), packed little-endian (common.hpp:
+// e4m3_quotient and the hardware conversion; r = fl32(1 / s)).
+__device__ __forceinline__ uint2 codes8(const float v[8], float s, float r, bool fast) {
+  float q[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(v[j] / s) << (8 * j);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) hi |= f32_to_e4m3(v[4 + j] / s) << (8 * j);
-  return make_uint2(lo, hi);
+  for (int j = 0; j < 8; ++j) q[j] = e4m3_quotient(v[j], s, r, fast);
+  return make_uint2(e4m3_pack4(q[0], q[1], q[2], q[3]), e4m3_pack4(q[4], q[5], q[6], q[7]));
 }
 
 __device__ __forceinline__ float block_max_ring(float v, float* red) {
@@ -338,10 +337,12 @@ void fused_decode_kernel(
     // ---- B: codes of x
     {
       const auto xr = dev_rsrc(xq);
+      const float rx = 1.0f / sx;
+      const bool fx = e4m3_fast_scale(sx, rx);
       for (size_t i = gtid * 8; i < nx; i += gthreads * 8) {
         float v[8];
         fused_load8<XT>(a.x, i, v);
-        coh_st8(xr, (uint32_t)i, codes8(v, sx));
+        coh_st8(xr, (uint32_t)i, codes8(v, sx, rx, fx));
       }
     }
     grid_barrier(sync, 1, epoch, -1.0f, a1_scale != nullptr || small_x, &bcast);
@@ -369,6 +370,8 @@ void fused_decode_kernel(
     const size_t rows = (size_t)(*a.num_padded), nh = rows * a.N;
     const auto hr = dev_rsrc(a.h);
     const auto qr = dev_rsrc(a.hq);
+    const float rh = 1.0f / sh;
+    const bool fh = e4m3_fast_scale(sh, rh);
     for (size_t i = gtid * 8; i < nh; i += gthreads * 8) {
       const size_t r = i / a.N, n = i - r * a.N;  // 8 columns of one 16-column block
       if (a.sorted_ids[r] >= a.P) continue;
@@ -380,7 +383,7 @@ void fused_decode_kernel(
         v[j] = __int_as_float(p[j]);
         v[4 + j] = __int_as_float(q[j]);
       }
-      coh_st8(qr, (uint32_t)i, codes8(v, sh));
+      coh_st8(qr, (uint32_t)i, codes8(v, sh, rh, fh));
     }
   }
   grid_barrier(sync, 3, epoch, -1.0f, false, &bcast);

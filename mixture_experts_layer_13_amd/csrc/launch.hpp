@@ -57,9 +57,10 @@ int launch_route_align(const float* logits, int M, int E, int k, int renorm, int
 int launch_quant_x(const void* x, int xt, size_t n, const float* static_scale,
                    float* partials, uint8_t* xq, float* sx, uint32_t* hmax_bits,
                    hipStream_t stream);
+// codes of the rows < *num_rows that hold a pair (sorted_ids[row] < P)
 int launch_quant_h(const float* h32, int N, int max_rows, const int32_t* num_rows,
-                   const uint32_t* hmax_bits, const float* static_scale,
-                   uint8_t* hq, float* sh, hipStream_t stream);
+                   const int32_t* sorted_ids, int P, const uint32_t* hmax_bits,
+                   const float* static_scale, uint8_t* hq, float* sh, hipStream_t stream);
 
 // Rotary embedding + per-head E4M3 quantisation (rope.hip); x [T, nH, D]
 // bf16 or f32, D % 16 == 0, nH <= 256; ws holds rope_workspace_bytes().

@@ -403,7 +403,8 @@ moe_status fused_forward(const moe_problem* p, const void* a, const void* w13, c
   if (prof[1]) (void)hipEventRecord((hipEvent_t)prof[1], st);
 
   if (fp8) {
-    err = moe::launch_quant_h((const float*)g.h, p->N, (int)cap, num_padded, g.hmax_bits,
+    err = moe::launch_quant_h((const float*)g.h, p->N, (int)cap, num_padded, sorted_pair_ids, g.P,
+                              g.hmax_bits,
                               a2_scale, (uint8_t*)(ws + L.hq), scal + 1, st);
     if (err) return hip_status(err, "intermediate quantisation launch");
     g.hq = ws + L.hq;

@@ -13,7 +13,9 @@
 //     s_x and the E4M3 codes of x.
 //   quant_x_one_kernel: the same for up to 1 MiB of x in one workgroup.
 //   quant_h_kernel: s_h from the running max (or a static scale), codes of
-//     the fp32 intermediate E4M3(fl32(h / s_h)), IEEE fp32 division.
+//     the fp32 intermediate E4M3(fl32(h / s_h)) of the real rows.
+// The codes: e4m3_quotient (common.hpp: the correctly rounded quotient
+// without a division per element) and the hardware conversion.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -39,6 +41,15 @@ __device__ __forceinline__ void load8(const void* x, size_t i, float v[8]) {
       v[4 + j] = __int_as_float(b[j]);
     }
   }
+}
+
+// Eight codes E4M3(fl32(v / s)), packed little-endian (r = fl32(1 / s),
+// fast = e4m3_fast_scale(s, r)).
+__device__ __forceinline__ uint2 e4m3_codes8(const float v[8], float s, float r, bool fast) {
+  float q[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) q[j] = e4m3_quotient(v[j], s, r, fast);
+  return make_uint2(e4m3_pack4(q[0], q[1], q[2], q[3]), e4m3_pack4(q[4], q[5], q[6], q[7]));
 }
 
 template <int NT = kQThreads>
@@ -102,16 +113,13 @@ __global__ __launch_bounds__(kQThreads) void quant_x_kernel(
     *sx_out = s;
     if (nparts == 0) *hmax_bits = 0u;
   }
+  const float r = 1.0f / s;
+  const bool fast = e4m3_fast_scale(s, r);
   for (size_t i = ((size_t)blockIdx.x * kQThreads + threadIdx.x) * 8; i < n;
        i += (size_t)gridDim.x * kQThreads * 8) {
     float v[8];
     load8<XT>(x, i, v);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(v[j] / s) << (8 * j);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hi |= f32_to_e4m3(v[4 + j] / s) << (8 * j);
-    *reinterpret_cast<uint2*>(xq + i) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(xq + i) = e4m3_codes8(v, s, r, fast);
   }
 }
 
@@ -152,23 +160,22 @@ __global__ __launch_bounds__(kQOneThreads) void quant_x_one_kernel(
     *sx_out = s;
     *hmax_bits = 0u;
   }
+  const float r = 1.0f / s;
+  const bool fast = e4m3_fast_scale(s, r);
   for (size_t k = (size_t)threadIdx.x * 8; k < n; k += kStep) {
     float v[8];
     load8<XT>(x, k, v);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(v[j] / s) << (8 * j);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hi |= f32_to_e4m3(v[4 + j] / s) << (8 * j);
-    *reinterpret_cast<uint2*>(xq + k) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(xq + k) = e4m3_codes8(v, s, r, fast);
   }
 }
 
-// h32: [rows, N] fp32; codes for rows < *num_rows.
+// h32: [rows, N] fp32; codes for the rows < *num_rows that hold a pair
+// (sorted_ids[row] < P): padding rows are neither read nor written (no
+// kernel uses their codes for an output).
 __global__ __launch_bounds__(kQThreads) void quant_h_kernel(
     const float* __restrict__ h32, int N, const int32_t* __restrict__ num_rows,
-    const uint32_t* __restrict__ hmax_bits, const float* __restrict__ static_scale,
-    uint8_t* __restrict__ hq, float* __restrict__ sh_out) {
+    const int32_t* __restrict__ sorted_ids, int P, const uint32_t* __restrict__ hmax_bits,
+    const float* __restrict__ static_scale, uint8_t* __restrict__ hq, float* __restrict__ sh_out) {
   float s;
   if (static_scale) {
     s = *static_scale;
@@ -177,16 +184,21 @@ __global__ __launch_bounds__(kQThreads) void quant_h_kernel(
     s = (m == 0.0f) ? 1.0f : m / 448.0f;
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) *sh_out = s;
+  const float r = 1.0f / s;
+  const bool fast = e4m3_fast_scale(s, r);
   const size_t n = (size_t)(*num_rows) * N;
   for (size_t i = ((size_t)blockIdx.x * kQThreads + threadIdx.x) * 8; i < n;
        i += (size_t)gridDim.x * kQThreads * 8) {
-    i32x4 a = ld16(h32 + i), b = ld16(h32 + i + 4);
-    uint32_t lo = 0, hi = 0;
+    const int f = sorted_ids[i / N];
+    if (f < 0 || f >= P) continue;
+    const i32x4 a = ld16(h32 + i), b = ld16(h32 + i + 4);
+    float v[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(__int_as_float(a[j]) / s) << (8 * j);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hi |= f32_to_e4m3(__int_as_float(b[j]) / s) << (8 * j);
-    *reinterpret_cast<uint2*>(hq + i) = make_uint2(lo, hi);
+    for (int j = 0; j < 4; ++j) {
+      v[j] = __int_as_float(a[j]);
+      v[4 + j] = __int_as_float(b[j]);
+    }
+    *reinterpret_cast<uint2*>(hq + i) = e4m3_codes8(v, s, r, fast);
   }
 }
 
@@ -232,14 +244,14 @@ int launch_quant_x(const void* x, int xt, size_t n, const float* static_scale,
 }
 
 int launch_quant_h(const float* h32, int N, int max_rows, const int32_t* num_rows,
-                   const uint32_t* hmax_bits, const float* static_scale, uint8_t* hq,
-                   float* sh, hipStream_t stream) {
+                   const int32_t* sorted_ids, int P, const uint32_t* hmax_bits,
+                   const float* static_scale, uint8_t* hq, float* sh, hipStream_t stream) {
   size_t n = (size_t)max_rows * N;
   const size_t per_wg = (size_t)kQThreads * 8;
   size_t want = (n + per_wg - 1) / per_wg;
   int g = (int)(want < 2048 ? (want ? want : 1) : 2048);
   hipLaunchKernelGGL(quant_h_kernel, dim3(g), dim3(kQThreads), 0, stream, h32, N,
-                     num_rows, hmax_bits, static_scale, hq, sh);
+                     num_rows, sorted_ids, P, hmax_bits, static_scale, hq, sh);
   return (int)hipGetLastError();
 }
 

@@ -30,18 +30,8 @@
 // With static scales only rope_quant_kernel runs.  T is only ever a kernel
 // argument.
 //
-// The codes: fl32(y / s_h) without a division per element, by Markstein's
-// correction step (P. Markstein, IBM J. Res. Dev. 34(1), 1990): with
-// r = fl32(1 / s_h) correctly rounded and q = fl32(y * r), the residual
-// e = y - s_h * q from one fused multiply-add and fl32(q + e * r) give the
-// correctly rounded quotient, except possibly within two ulps of a power of
-// two, where the residual can need one bit more than binary32 holds; powers
-// of two are E4M3 values, not rounding midpoints, so the E4M3 code is that of
-// the correctly rounded quotient in every case.  Quotients beyond 1024 in
-// magnitude keep q (their code saturates whatever the last bits).  The code
-// of the clamped quotient comes from v_cvt_pk_fp8_f32, which rounds to
-// nearest even like the software encoder (checked equal on every E4M3
-// midpoint, its neighbours and a dense sample of the fp32 range).
+// The codes: e4m3_quotient (common.hpp: the correctly rounded quotient
+// without a division per element) and the hardware conversion.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -136,27 +126,15 @@ __device__ __forceinline__ void rope_rotate(const i32x4 raw[4], int g, const flo
   }
 }
 
-// fl32(y / s), clamped to +-448, as described at the top (r = fl32(1 / s)).
-__device__ __forceinline__ float rope_quotient(float y, float s, float r) {
-  const float q0 = y * r;
-  const float e = __builtin_fmaf(-q0, s, y);
-  const float q1 = __builtin_fmaf(e, r, q0);
-  const float q = __builtin_fabsf(q0) < 1024.0f ? q1 : q0;
-  return __builtin_fminf(__builtin_fmaxf(q, -448.0f), 448.0f);
-}
-
 template <bool IL>
 __device__ __forceinline__ void rope_store(const RopeArgs& a, int t, int h, int g, const float y[16],
                                            float s, float r) {
+  const bool fast = e4m3_fast_scale(s, r);
   uint32_t w[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int v = __builtin_amdgcn_cvt_pk_fp8_f32(rope_quotient(y[4 * j], s, r),
-                                            rope_quotient(y[4 * j + 1], s, r), 0, false);
-    v = __builtin_amdgcn_cvt_pk_fp8_f32(rope_quotient(y[4 * j + 2], s, r),
-                                        rope_quotient(y[4 * j + 3], s, r), v, true);
-    w[j] = (uint32_t)v;
-  }
+  for (int j = 0; j < 4; ++j)
+    w[j] = e4m3_pack4(e4m3_quotient(y[4 * j], s, r, fast), e4m3_quotient(y[4 * j + 1], s, r, fast),
+                      e4m3_quotient(y[4 * j + 2], s, r, fast), e4m3_quotient(y[4 * j + 3], s, r, fast));
   uint8_t* row = a.codes + ((size_t)t * a.nH + h) * a.D;
   if (IL) {
     *reinterpret_cast<uint4*>(row + 16 * g) = make_uint4(w[0], w[1], w[2], w[3]);

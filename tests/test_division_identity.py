@@ -1,13 +1,16 @@
-"""The RoPE quantiser forms fl32(y / s) without a division per element:
-q = fl32(y * r) with r = fl32(1 / s), the residual e = fl32(y - s q) (one
-fused multiply-add), then fl32(q + e r) -- Markstein's correction step.  This
-checks, in exact rational arithmetic on the CPU, that the E4M3 code of the
-result always equals that of the correctly rounded quotient, and that the
-result is the correctly rounded quotient itself except, at most, within two
-ulps of a power of two (where the residual may need one bit more than binary32
-holds; powers of two are E4M3 values, never rounding midpoints), on random
-pairs, divisors whose significands are all ones or all zeros and quotients
-next to E4M3 rounding midpoints."""
+"""The E4M3 quantisers (activations, the intermediate h, RoPE) form
+fl32(y / s) without a division per element: q = fl32(y * r) with
+r = fl32(1 / s), the residual e = fl32(y - s q) (one fused multiply-add), then
+fl32(q + e r) -- Markstein's correction step -- and an IEEE division only for
+quotients within four ulps of 2^-10, the one power of two that is an E4M3
+rounding midpoint (between 0 and the smallest subnormal 2^-9).  This checks,
+in exact rational arithmetic on the CPU, that the E4M3 code of the result
+always equals that of the correctly rounded quotient, and that the result is
+the correctly rounded quotient itself except, at most, within two ulps of a
+power of two (where the residual may need one bit more than binary32 holds),
+on random pairs, divisors whose significands are all ones or all zeros,
+quotients next to E4M3 rounding midpoints and quotients next to powers of
+two, 2^-10 among them."""
 import random
 from fractions import Fraction as Fr
 
@@ -56,3 +59,39 @@ def test_markstein_step_gives_the_correctly_rounded_quotient():
             assert abs(float(want) - p2) <= 2 * abs(float(np.spacing(np.float32(p2)))), (y, s, q1, want)
             misses += 1
     assert misses <= 20000 // 1000
+
+
+def _kernel_quotient(y, s):
+    """The kernels' quotient (common.hpp e4m3_quotient before the clamp), in
+    exact arithmetic: the correction step, q itself beyond 1024, the IEEE
+    quotient within four ulps of 2^-10, the sign of y."""
+    Y, S = Fr(float(y)), Fr(float(s))
+    r = _rn32(1 / S)
+    q0 = _rn32(Y * Fr(float(r)))
+    e = _rn32(Y - S * Fr(float(q0)))
+    q = _rn32(Fr(float(e)) * Fr(float(r)) + Fr(float(q0)))
+    if abs(float(q0)) >= 1024.0:
+        q = q0
+    if abs((_bits(q) & 0x7FFFFFFF) - _bits(np.float32(2.0 ** -10))) <= 4:
+        q = _rn32(Y / S)
+    return np.float32(np.copysign(float(q), float(y)))
+
+
+def test_quotient_next_to_powers_of_two_and_the_subnormal_midpoint():
+    """Quotients within two ulps of 2^-10 (an E4M3 midpoint: ties go to the
+    even code 0), 2^-9, 2^-3 and 1, over divisors with random significands:
+    the code always equals that of the correctly rounded quotient; -0 keeps
+    its sign."""
+    rng = random.Random(11)
+    for p in (2.0 ** -10, 2.0 ** -9, 2.0 ** -3, 1.0):
+        for _ in range(1500):
+            s = _from_bits((rng.randrange(100, 140) << 23) | rng.randrange(0, 1 << 23))
+            y0 = _bits(np.float32(p * float(s)))
+            for k in (-2, -1, 0, 1, 2):
+                y = _from_bits(y0 + k)
+                want = _rn32(Fr(float(y)) / Fr(float(s)))
+                got = _kernel_quotient(y, s)
+                assert oracle.e4m3_from_f32(float(got)) == oracle.e4m3_from_f32(float(want)), (p, y, s)
+    s = np.float32(0.37)
+    assert _bits(_kernel_quotient(np.float32(-0.0), s)) == 0x80000000
+    assert oracle.e4m3_from_f32(float(_kernel_quotient(np.float32(-0.0), s))) == 0x80
