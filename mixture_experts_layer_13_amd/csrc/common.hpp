@@ -67,7 +67,7 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
   return sign | (e << 3) | ((r >> 20) & 7u);
 }
 
-// Whether e4m3_quotient may use the reciprocal of the scale s.
+// Whether e4m3_codes4 may use the reciprocal of the scale s.
 __device__ __forceinline__ bool e4m3_fast_scale(float s, float r) {
   return s >= 1.17549435e-38f && r <= 3.40282347e+38f;
 }
@@ -79,33 +79,40 @@ __device__ __forceinline__ bool e4m3_fast_scale(float s, float r) {
 // q = fl32(y r), the residual e = y - s q from one fused multiply-add (exact),
 // and fl32(q + e r) is the correctly rounded quotient, except possibly within
 // two ulps of a power of two, where the residual can need one bit more than
-// binary32 holds.  Powers of two are E4M3 values, not rounding midpoints --
-// all but 2^-10, the midpoint between 0 and the smallest subnormal 2^-9: a
-// quotient within four ulps of it takes the IEEE division instead.  So the
-// code is that of the correctly rounded quotient in every case.  Quotients
-// beyond 1024 in magnitude keep q (their code saturates whatever the last
-// bits); the sign is y's (so -0 keeps its sign).  The result is clamped to
-// +-448 (a NaN y gives a saturated code, not the NaN code).
-__device__ __forceinline__ float e4m3_quotient(float y, float s, float r, bool fast) {
-  const float q0 = y * r;
-  const float e = __builtin_fmaf(-q0, s, y);
-  float q = __builtin_fmaf(e, r, q0);
-  if (__builtin_fabsf(q0) >= 1024.0f) q = q0;
-  const uint32_t d = (__float_as_uint(q) & 0x7fffffffu) - 0x3a800000u;  // 2^-10
-  if (__builtin_expect(d + 4u <= 8u || !fast, 0)) q = y / s;
-  q = __builtin_copysignf(q, y);
-  return __builtin_fminf(__builtin_fmaxf(q, -448.0f), 448.0f);
-}
-
-// Four E4M3 codes (little-endian) of values already in [-448, 448], by the
-// hardware conversion, which rounds to nearest even like f32_to_e4m3 (checked
-// equal on every E4M3 midpoint, its neighbours and a dense sample of the
-// fp32 range).
-__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
-  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+// binary32 holds.  From 2^-9 (the smallest E4M3 subnormal) up, powers of two
+// are E4M3 values, not rounding midpoints, so there the code is that of the
+// correctly rounded quotient.  Below 2^-9 lies 2^-10, the midpoint between 0
+// and 2^-9: a group of four with a quotient under 2^-9 (zeros among them,
+// which so keep their sign) takes the IEEE division for all four, one branch
+// per group, and so does a group with an infinite y (its corrected quotient
+// is NaN).  Quotients of 448 and more saturate, whatever their last bits.
+// The codes come from the hardware
+// conversion of the quotient clamped to +-448, which rounds to nearest even
+// like f32_to_e4m3 (checked equal on every E4M3 midpoint, its neighbours and
+// a dense sample of the fp32 range); a NaN y gives a saturated code, not the
+// NaN code.  Four codes, little-endian.
+__device__ __forceinline__ uint32_t e4m3_codes4(float y0, float y1, float y2, float y3, float s, float r,
+                                                bool fast) {
+  float y[4] = {y0, y1, y2, y3}, q[4];
+  bool slow = !fast;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float q0 = y[j] * r;
+    const float e = __builtin_fmaf(-q0, s, y[j]);
+    q[j] = __builtin_fmaf(e, r, q0);
+    slow |= !(__builtin_fabsf(q[j]) >= 0x1p-9f);
+  }
+  if (__builtin_expect(slow, 0)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) q[j] = y[j] / s;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) q[j] = __builtin_fminf(__builtin_fmaxf(q[j], -448.0f), 448.0f);
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], v, true);
   return (uint32_t)v;
 }
+
 
 // ----------------------------------------------------------------- memory
 

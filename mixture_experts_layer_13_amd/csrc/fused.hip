@@ -170,13 +170,10 @@ __device__ __forceinline__ void fused_load8(const void* x, size_t i, float v[8])
   }
 }
 
-// Eight codes E4M3(fl32(v / s)), packed little-endian (common.hpp:
-// e4m3_quotient and the hardware conversion; r = fl32(1 / s)).
+// Eight codes E4M3(fl32(v / s)), packed little-endian (common.hpp
+// e4m3_codes4; r = fl32(1 / s)).
 __device__ __forceinline__ uint2 codes8(const float v[8], float s, float r, bool fast) {
-  float q[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) q[j] = e4m3_quotient(v[j], s, r, fast);
-  return make_uint2(e4m3_pack4(q[0], q[1], q[2], q[3]), e4m3_pack4(q[4], q[5], q[6], q[7]));
+  return make_uint2(e4m3_codes4(v[0], v[1], v[2], v[3], s, r, fast), e4m3_codes4(v[4], v[5], v[6], v[7], s, r, fast));
 }
 
 __device__ __forceinline__ float block_max_ring(float v, float* red) {

@@ -14,8 +14,8 @@
 //   quant_x_one_kernel: the same for up to 1 MiB of x in one workgroup.
 //   quant_h_kernel: s_h from the running max (or a static scale), codes of
 //     the fp32 intermediate E4M3(fl32(h / s_h)) of the real rows.
-// The codes: e4m3_quotient (common.hpp: the correctly rounded quotient
-// without a division per element) and the hardware conversion.
+// The codes: e4m3_codes4 (common.hpp: the correctly rounded quotient
+// without a division per element, the hardware conversion).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -46,10 +46,7 @@ __device__ __forceinline__ void load8(const void* x, size_t i, float v[8]) {
 // Eight codes E4M3(fl32(v / s)), packed little-endian (r = fl32(1 / s),
 // fast = e4m3_fast_scale(s, r)).
 __device__ __forceinline__ uint2 e4m3_codes8(const float v[8], float s, float r, bool fast) {
-  float q[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) q[j] = e4m3_quotient(v[j], s, r, fast);
-  return make_uint2(e4m3_pack4(q[0], q[1], q[2], q[3]), e4m3_pack4(q[4], q[5], q[6], q[7]));
+  return make_uint2(e4m3_codes4(v[0], v[1], v[2], v[3], s, r, fast), e4m3_codes4(v[4], v[5], v[6], v[7], s, r, fast));
 }
 
 template <int NT = kQThreads>

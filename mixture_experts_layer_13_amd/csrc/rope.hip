@@ -30,8 +30,8 @@
 // With static scales only rope_quant_kernel runs.  T is only ever a kernel
 // argument.
 //
-// The codes: e4m3_quotient (common.hpp: the correctly rounded quotient
-// without a division per element) and the hardware conversion.
+// The codes: e4m3_codes4 (common.hpp: the correctly rounded quotient
+// without a division per element, the hardware conversion).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -133,8 +133,7 @@ __device__ __forceinline__ void rope_store(const RopeArgs& a, int t, int h, int 
   uint32_t w[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    w[j] = e4m3_pack4(e4m3_quotient(y[4 * j], s, r, fast), e4m3_quotient(y[4 * j + 1], s, r, fast),
-                      e4m3_quotient(y[4 * j + 2], s, r, fast), e4m3_quotient(y[4 * j + 3], s, r, fast));
+    w[j] = e4m3_codes4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3], s, r, fast);
   uint8_t* row = a.codes + ((size_t)t * a.nH + h) * a.D;
   if (IL) {
     *reinterpret_cast<uint4*>(row + 16 * g) = make_uint4(w[0], w[1], w[2], w[3]);

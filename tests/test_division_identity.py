@@ -2,8 +2,9 @@
 fl32(y / s) without a division per element: q = fl32(y * r) with
 r = fl32(1 / s), the residual e = fl32(y - s q) (one fused multiply-add), then
 fl32(q + e r) -- Markstein's correction step -- and an IEEE division only for
-quotients within four ulps of 2^-10, the one power of two that is an E4M3
-rounding midpoint (between 0 and the smallest subnormal 2^-9).  This checks,
+groups of four values with a quotient under 2^-9, the smallest E4M3 subnormal
+(below it lie 2^-10, the one power of two that is an E4M3 rounding midpoint,
+and zero).  This checks,
 in exact rational arithmetic on the CPU, that the E4M3 code of the result
 always equals that of the correctly rounded quotient, and that the result is
 the correctly rounded quotient itself except, at most, within two ulps of a
@@ -62,19 +63,21 @@ def test_markstein_step_gives_the_correctly_rounded_quotient():
 
 
 def _kernel_quotient(y, s):
-    """The kernels' quotient (common.hpp e4m3_quotient before the clamp), in
-    exact arithmetic: the correction step, q itself beyond 1024, the IEEE
-    quotient within four ulps of 2^-10, the sign of y."""
+    """The kernels' quotient (common.hpp e4m3_codes4 before the clamp), in
+    exact arithmetic, one value at a time: the correction step, the IEEE
+    quotient under 2^-9 in magnitude.  (The kernels
+    divide all four values of a group that holds such a quotient; the others
+    then take the correctly rounded quotient, whose code is the same.)"""
     Y, S = Fr(float(y)), Fr(float(s))
     r = _rn32(1 / S)
     q0 = _rn32(Y * Fr(float(r)))
     e = _rn32(Y - S * Fr(float(q0)))
     q = _rn32(Fr(float(e)) * Fr(float(r)) + Fr(float(q0)))
-    if abs(float(q0)) >= 1024.0:
-        q = q0
-    if abs((_bits(q) & 0x7FFFFFFF) - _bits(np.float32(2.0 ** -10))) <= 4:
+    if not abs(float(q)) >= 2.0 ** -9:
         q = _rn32(Y / S)
-    return np.float32(np.copysign(float(q), float(y)))
+        if float(q) == 0.0:
+            q = np.float32(np.copysign(0.0, float(y)))  # IEEE: the sign of y / s
+    return np.float32(q)
 
 
 def test_quotient_next_to_powers_of_two_and_the_subnormal_midpoint():
