@@ -61,7 +61,8 @@ def parse():
     ap.add_argument("--persistent", action="store_true",
                     help="E4M3 decode: run the forward as one launch (moe_fused_forward_persistent)")
     ap.add_argument("--in-kernel-x", action="store_true",
-                    help="with --persistent: quantise x inside the one launch instead of beside the routing")
+                    help="with --persistent: quantise x inside the one launch instead of beside the "
+                         "routing")
     ap.add_argument("--copy-check", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -343,7 +344,8 @@ def main():
     H, I, E, k = d["H"], d["I"], d["E"], d["topk"]
     layer = moe.FusedMoE(T, H, I, E, k, d["w13"], d["w2"], d["w13_scale"], d["w2_scale"],
                          a_dtype=wl.x_dtype, out_dtype=wl.out_dtype, device=dev,
-                         persistent=args.persistent, prequant=not args.in_kernel_x)
+                         persistent=args.persistent,
+                         prequant=False if args.in_kernel_x else None)
     x, logits = d["x"], d["logits"]
 
     ev = HipEvents()
@@ -366,9 +368,7 @@ def main():
         flush.fill_(i & 0xFF)
         ev.record(sev[2 * i], st.cuda_stream)
         if args.persistent:  # the one launch of the forward between the kernel events
-            layer.route(logits)
-            if layer.prequant:
-                layer.quantize(x)
+            layer.prepare(x, logits)
             ev.record(kev[4 * i], st.cuda_stream)
             layer.forward(x)
             ev.record(kev[4 * i + 1], st.cuda_stream)
@@ -478,8 +478,9 @@ def main():
     roof["algorithmic_bytes_per_launch"] = int(g1_bytes)
     src_sha = kernel_source_sha()
     key = f"{args.workload}:T{T}" + (":persistent" if args.persistent else "")
-    if args.persistent:
-        roof["x_quantised"] = "inside the launch" if args.in_kernel_x else "beside the routing (moe_quantize_act)"
+    if fp8:
+        roof["x_quantised"] = ("beside the routing (moe_quantize_act)" if layer.prequant
+                               else "inside the launch" if args.persistent else "by the forward")
     if os.path.exists(PMC_FILE):
         rec = json.load(open(PMC_FILE)).get(key)
         if rec and rec.get("gemm_source_sha256") == src_sha:

@@ -73,7 +73,10 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
  *   E        experts, 1..1024.
  *   topk     experts per token, 1..min(E, 64).
  *   block_m  segment padding used by moe_align_permute: 16, 32, 64, 128, 256.
- *   a_dtype  activations x: MOE_F32 or MOE_BF16.
+ *   a_dtype  activations x: MOE_F32 or MOE_BF16; or, with E4M3 weights,
+ *            MOE_FP8_E4M3: codes made beforehand (moe_quantize_act), their
+ *            scale s_x in a1_scale (required), so that the quantisation can
+ *            run beside the routing.
  *   w_dtype  weights: MOE_F32, MOE_BF16 (computed on bf16 MFMA, fp32
  *            accumulate; f32 values are rounded to bf16 on load) or
  *            MOE_FP8_E4M3 (OCP E4M3FN codes with one fp32 scale per expert
@@ -231,7 +234,8 @@ moe_status moe_route_project_workspace_size(int32_t M, int32_t K, int32_t E, siz
  *        (must not alias any input).
  * w13_scale, w2_scale  device f32 [E]; required for E4M3 weights, else NULL.
  * a1_scale, a2_scale   device f32 [1] static scales or NULL (dynamic); only
- *        read for E4M3 weights.
+ *        read for E4M3 weights.  With E4M3 activations a1_scale is required
+ *        and is their scale s_x (the x quantisation is then skipped).
  * topk_weights         device f32 [M, topk] from moe_route_topk.
  * sorted_pair_ids, block_expert_ids, expert_offsets, pair_pos, num_padded
  *        device int32, from moe_align_permute with the same M, topk, E and

@@ -57,6 +57,8 @@ int launch_route_align(const float* logits, int M, int E, int k, int renorm, int
 int launch_quant_x(const void* x, int xt, size_t n, const float* static_scale,
                    float* partials, uint8_t* xq, float* sx, uint32_t* hmax_bits,
                    hipStream_t stream);
+// pre-quantised activations: s_x = *a1_scale into sx, running max of |h| = 0
+int launch_fwd_prequant(const float* a1_scale, float* sx, uint32_t* hmax_bits, hipStream_t stream);
 // codes of the rows < *num_rows that hold a pair (sorted_ids[row] < P)
 int launch_quant_h(const float* h32, int N, int max_rows, const int32_t* num_rows,
                    const int32_t* sorted_ids, int P, const uint32_t* hmax_bits,

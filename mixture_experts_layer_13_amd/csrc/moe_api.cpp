@@ -287,14 +287,10 @@ moe_status fused_forward(const moe_problem* p, const void* a, const void* w13, c
   moe_status s = check_problem(p);
   if (s) return s;
   if (p->M == 0) return ok();
-  if (p->a_dtype == MOE_FP8_E4M3 && !persistent)
-    return fail(MOE_ERR_UNSUPPORTED,
-                "activations must be f32 or bf16 (FP8 quantisation is internal; pre-quantised "
-                "codes only in moe_fused_forward_persistent)");
+  if (p->a_dtype == MOE_FP8_E4M3 && !a1_scale)
+    return fail(MOE_ERR_NULL, "E4M3 activations need their scale in a1_scale");
   if (persistent) {
     if (!sync) return fail(MOE_ERR_NULL, "sync is NULL");
-    if (p->a_dtype == MOE_FP8_E4M3 && !a1_scale)
-      return fail(MOE_ERR_NULL, "E4M3 activations need their scale in a1_scale");
     if (!aligned(sync, 128)) return fail(MOE_ERR_ALIGN, "sync must be 128-byte aligned");
     if (sync_bytes < MOE_FUSED_SYNC_BYTES)
       return fail(MOE_ERR_WORKSPACE, "sync buffer of %d bytes needed, %zu given",
@@ -378,7 +374,13 @@ moe_status fused_forward(const moe_problem* p, const void* a, const void* w13, c
     if (err) return hip_status(err, "one-launch forward");
     return ok();
   }
-  if (fp8) {
+  if (fp8 && p->a_dtype == MOE_FP8_E4M3) {
+    // codes made beforehand (moe_quantize_act), their scale in a1_scale
+    err = moe::launch_fwd_prequant(a1_scale, scal + 0, g.hmax_bits, st);
+    if (err) return hip_status(err, "pre-quantised activation launch");
+    g.x = a;
+    g.xt = MOE_FP8_E4M3;
+  } else if (fp8) {
     err = moe::launch_quant_x(a, p->a_dtype, (size_t)p->M * p->K, a1_scale,
                               (float*)(ws + L.partials), (uint8_t*)(ws + L.xq), scal + 0,
                               g.hmax_bits, st);

@@ -199,6 +199,22 @@ __global__ __launch_bounds__(kQThreads) void quant_h_kernel(
   }
 }
 
+// Activations quantised beforehand (their codes and scale s_x come in):
+// s_x into the forward's scalar and the running max of |h| cleared.
+__global__ __launch_bounds__(64) void fwd_prequant_kernel(const float* __restrict__ a1_scale,
+                                                          float* __restrict__ sx,
+                                                          uint32_t* __restrict__ hmax_bits) {
+  if (threadIdx.x == 0) {
+    *sx = *a1_scale;
+    *hmax_bits = 0u;
+  }
+}
+
+int launch_fwd_prequant(const float* a1_scale, float* sx, uint32_t* hmax_bits, hipStream_t stream) {
+  hipLaunchKernelGGL(fwd_prequant_kernel, dim3(1), dim3(64), 0, stream, a1_scale, sx, hmax_bits);
+  return (int)hipGetLastError();
+}
+
 int launch_quant_x(const void* x, int xt, size_t n, const float* static_scale,
                    float* partials, uint8_t* xq, float* sx, uint32_t* hmax_bits,
                    hipStream_t stream) {

@@ -333,7 +333,7 @@ class FusedMoE:
     def __init__(self, M, K, N, E, topk, w13, w2, w13_scale=None, w2_scale=None,
                  block_m=None, a_dtype=torch.bfloat16, out_dtype=torch.bfloat16,
                  renormalize=True, a1_scale=None, a2_scale=None, device="cuda",
-                 persistent=False, prequant=True):
+                 persistent=False, prequant=None):
         if block_m is None:
             # alignment block: 16 rows for decode-sized batches (the stream and
             # ring kernels), 256 once the experts average 512 rows or more (the
@@ -351,11 +351,15 @@ class FusedMoE:
         self.alignment = alloc_alignment(M, topk, E, block_m, device)
         self.out = torch.empty(M, K, dtype=out_dtype, device=device)
         # persistent: the forward runs as one launch (moe_fused_forward_persistent);
-        # prequant: the activation codes are made first (moe_quantize_act,
-        # next to the routing), and the one launch starts at gate/up
+        # prequant (E4M3 weights; default: with the one launch only): the
+        # activation codes are made by moe_quantize_act right after the
+        # routing, and the forward starts from them (the one launch then
+        # starts at gate/up)
         self.persistent = persistent
         self.sync = alloc_fused_sync(device) if persistent else None
-        self.prequant = persistent and prequant and w13.dtype == torch.float8_e4m3fn
+        if prequant is None:
+            prequant = persistent
+        self.prequant = bool(prequant) and w13.dtype == torch.float8_e4m3fn
         if self.prequant:
             self.problem_q = make_problem(M, K, N, E, topk, block_m, torch.float8_e4m3fn,
                                           w13.dtype, out_dtype)
@@ -370,10 +374,14 @@ class FusedMoE:
         return self.workspace[o:o + 8].view(torch.float32)
 
     def __call__(self, x, logits, stream=None, events=None):
+        self.prepare(x, logits, stream)
+        return self.forward(x, stream, events)
+
+    def prepare(self, x, logits, stream=None):
+        """Routing and alignment; in prequant mode then the activation codes."""
         self.route(logits, stream)
         if self.prequant:
             self.quantize(x, stream)
-        return self.forward(x, stream, events)
 
     def route(self, logits, stream=None):
         moe_route_align(logits, self.topk, self.renormalize, self.block_m, self.workspace,
@@ -384,11 +392,15 @@ class FusedMoE:
         moe_quantize_act(x, self.a1_scale, self.xq, self.xscale, self.qws, stream)
 
     def forward(self, x, stream=None, events=None):
-        if self.prequant:
+        if self.prequant and self.persistent:
             moe_fused_forward_persistent(self.problem_q, self.xq, self.w13, self.w2,
                                          self.topk_weights, self.alignment, self.out,
                                          self.workspace, self.sync, self.w13_scale,
                                          self.w2_scale, self.xscale, self.a2_scale, stream)
+        elif self.prequant:
+            moe_fused_forward(self.problem_q, self.xq, self.w13, self.w2, self.topk_weights,
+                              self.alignment, self.out, self.workspace, self.w13_scale,
+                              self.w2_scale, self.xscale, self.a2_scale, stream, events)
         elif self.persistent:
             moe_fused_forward_persistent(self.problem, x, self.w13, self.w2, self.topk_weights,
                                          self.alignment, self.out, self.workspace, self.sync,

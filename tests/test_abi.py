@@ -171,6 +171,11 @@ def test_forward_rejects_without_launch():
     assert _fwd(p, out=FAKE) == moe.MOE_ERR_SHAPE  # out aliases x
     # M == 0 passes validation and launches nothing
     assert _fwd(_prob(M=0)) == moe.MOE_OK
+    # pre-quantised (E4M3) activations: only with E4M3 weights, and with their scale
+    e4 = moe.MOE_FP8_E4M3
+    assert _fwd(_prob(a_dtype=e4)) == moe.MOE_ERR_UNSUPPORTED  # bf16 weights
+    assert _fwd(_prob(a_dtype=e4, w_dtype=e4), s13=FAKE, s2=FAKE) == moe.MOE_ERR_NULL
+    assert "a1_scale" in moe.moe_last_error()
 
 
 def test_quantize_rejects_without_launch():
@@ -311,6 +316,6 @@ def test_persistent_forward_rejects_without_launch():
     assert call(bm=32) == moe.MOE_ERR_UNSUPPORTED  # 16-row blocks only
     assert call(M=65) == moe.MOE_ERR_UNSUPPORTED   # decode batches only
     assert call(M=0, sync=0) == moe.MOE_OK        # empty batch: no-op
-    # pre-quantised activations: only with E4M3 weights, only here, and with their scale
+    # pre-quantised activations: only with E4M3 weights, and with their scale
     assert call(a=e4) == moe.MOE_ERR_NULL and "a1_scale" in moe.moe_last_error()
     assert call(a=e4, w=bf) == moe.MOE_ERR_UNSUPPORTED

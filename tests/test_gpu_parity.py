@@ -452,3 +452,60 @@ def test_forward_full_size_sampled_tokens(wl, T):
     o = out.float()
     assert torch.isfinite(o).all()
     assert (o.abs().amax(dim=1) > 0).all()
+
+
+# ------------------------------------------- pre-quantised activations
+
+PREQUANT = [("decode_fp8", 1, {}), ("decode_fp8", 3, {}), ("decode_fp8", 8, {}),
+            ("decode_fp8", 64, {}), ("large_fp8", 256, {}),
+            ("prefill_fp8", 1100, dict(H=768, I=512, E=8, topk=4))]
+
+
+@pytest.mark.parametrize("wl,T,shape", PREQUANT, ids=[f"{c[0]}_T{c[1]}" for c in PREQUANT])
+def test_prequantised_activations_equal_internal_quantisation(wl, T, shape):
+    """E4M3 codes made beforehand by moe_quantize_act and handed to
+    moe_fused_forward with their scale give the same s_x, s_h and output,
+    bit for bit, as the forward that quantises x itself (the same codes from
+    the same kernels)."""
+    w = W[wl]
+    d = inputs.make_inputs(w, T, device=DEV, seed=300 + T, **shape)
+    outs = []
+    for pre in (False, True):
+        layer = moe.FusedMoE(T, d["H"], d["I"], d["E"], d["topk"], d["w13"], d["w2"], d["w13_scale"],
+                             d["w2_scale"], a_dtype=d["x"].dtype, out_dtype=w.out_dtype, device=DEV,
+                             prequant=pre)
+        assert layer.prequant == pre
+        outs.append((layer(d["x"], d["logits"]).clone(), layer.act_scales().clone()))
+        torch.cuda.synchronize()
+    H.say(f"  {wl} T={T}: scales {outs[0][1].tolist()} / {outs[1][1].tolist()}")
+    assert torch.equal(outs[0][1], outs[1][1])
+    assert torch.equal(outs[0][0], outs[1][0])
+
+
+def test_prequantised_step_in_a_graph():
+    """The step with pre-quantised activations (routing, codes, forward)
+    captured once and replayed with eager work in between: every replay
+    equals the eager step."""
+    w = W["decode_fp8"]
+    T = 16
+    d = inputs.make_inputs(w, T, device=DEV, seed=44)
+    layer = moe.FusedMoE(T, w.H, w.I, w.E, w.topk, d["w13"], d["w2"], d["w13_scale"], d["w2_scale"],
+                         a_dtype=d["x"].dtype, out_dtype=w.out_dtype, device=DEV, prequant=True)
+    assert layer.prequant
+    eager = layer(d["x"], d["logits"]).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            layer(d["x"], d["logits"], stream=s)
+    torch.cuda.synchronize()
+    for r in range(3):
+        layer.out.zero_()
+        layer.xq.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.out, eager), r
+    del g
