@@ -226,7 +226,7 @@ moe_status moe_route_project_workspace_size(int32_t M, int32_t K, int32_t E, siz
  *   x codes = E4M3(fl32(x / s_x)), round to nearest even, saturating;
  *   GEMM1 output scaled by s_x * w13_scale[e];
  *   s_h = a2_scale ? *a2_scale : fl32(amax|h| / 448) over all real pairs,
- *   h codes = E4M3(fl32(h / s_h)), IEEE fp32 division;
+ *   h codes = E4M3(fl32(h / s_h)), the correctly rounded fp32 quotient;
  *   GEMM2 output scaled by s_h * w2_scale[e].
  *
  * a      device [M, K] of a_dtype.       w13  device [E, 2N, K] of w_dtype.
@@ -257,7 +257,7 @@ moe_status moe_fused_forward(
  * can check the codes bit for bit).  Per-tensor scaling as in [post],
  * "Backend routing for FP8 tensor quantization":
  *   *scale = static_scale ? *static_scale : fl32(amax|x| / 448) (1 if 0);
- *   codes[i] = E4M3(fl32(x[i] / *scale)), IEEE fp32 division, round to
+ *   codes[i] = E4M3(fl32(x[i] / *scale)) (the correctly rounded fp32 quotient), round to
  *   nearest even, saturating at +-448 (OCP E4M3FN).
  * x          device [n] of x_dtype (MOE_F32 or MOE_BF16), 16-byte aligned.
  * n          element count, a multiple of 128, >= 0.

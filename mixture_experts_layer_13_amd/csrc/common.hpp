@@ -49,24 +49,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
 }
 
-// binary32 -> OCP E4M3FN code: round to nearest even, saturate to +-448,
-// NaN -> 0x7F.  Normal E4M3 values have 3 fraction bits, so rounding the
-// binary32 significand to 3 bits (ties to even) and rebasing the exponent
-// from bias 127 to bias 7 gives the code; below 2^-6 the spacing is a fixed
-// 2^-9, so the code is rint(|f| * 2^9).
-__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
-  uint32_t u = __float_as_uint(f);
-  uint32_t sign = (u >> 24) & 0x80u;
-  float a = __builtin_fabsf(f);
-  if (!(a == a)) return 0x7fu;
-  if (a >= 448.0f) return sign | 0x7eu;
-  if (a < 0.015625f) return sign | (uint32_t)__builtin_rintf(a * 512.0f);
-  uint32_t ua = __float_as_uint(a);
-  uint32_t r = (ua + 0x7ffffu + ((ua >> 20) & 1u)) & 0xfff00000u;
-  uint32_t e = ((r >> 23) & 0xffu) - 120u;  // (exp - 127) + 7
-  return sign | (e << 3) | ((r >> 20) & 7u);
-}
-
 // Whether e4m3_codes4 may use the reciprocal of the scale s.
 __device__ __forceinline__ bool e4m3_fast_scale(float s, float r) {
   return s >= 1.17549435e-38f && r <= 3.40282347e+38f;
@@ -87,10 +69,10 @@ __device__ __forceinline__ bool e4m3_fast_scale(float s, float r) {
 // per group, and so does a group with an infinite y (its corrected quotient
 // is NaN).  Quotients of 448 and more saturate, whatever their last bits.
 // The codes come from the hardware
-// conversion of the quotient clamped to +-448, which rounds to nearest even
-// like f32_to_e4m3 (checked equal on every E4M3 midpoint, its neighbours and
-// a dense sample of the fp32 range); a NaN y gives a saturated code, not the
-// NaN code.  Four codes, little-endian.
+// conversion of the quotient clamped to +-448 (OCP E4M3FN, round to nearest
+// even: equal to the IEEE reading at every E4M3 rounding midpoint and its
+// fp32 neighbours, both signs, for exact and inexact quotients); a NaN y
+// gives a saturated code, not the NaN code.  Four codes, little-endian.
 __device__ __forceinline__ uint32_t e4m3_codes4(float y0, float y1, float y2, float y3, float s, float r,
                                                 bool fast) {
   float y[4] = {y0, y1, y2, y3}, q[4];

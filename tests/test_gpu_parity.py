@@ -509,3 +509,37 @@ def test_prequantised_step_in_a_graph():
         torch.cuda.synchronize()
         assert torch.equal(layer.out, eager), r
     del g
+
+
+def _e4m3_positive_values():
+    """The 127 non-negative finite E4M3FN values, ascending."""
+    return np.array(sorted({float(oracle.e4m3_to_f64(c)) for c in range(0x7F)}), np.float64)
+
+
+@pytest.mark.parametrize("s", [1.0, 0.37, 3.0e-3])
+def test_quantize_codes_at_every_e4m3_midpoint(s):
+    """Every rounding midpoint between adjacent E4M3 values (2^-10 between
+    0 and the smallest subnormal among them), times the scale, and its fp32
+    neighbours, both signs, plus values past saturation: the codes of the
+    corrected-reciprocal quotient and the hardware conversion equal the
+    oracle's E4M3(fl32(x / s)) with an IEEE division, bit for bit.  With
+    s = 1 every quotient is exact (the conversion alone is pinned)."""
+    v = _e4m3_positive_values()
+    mids = (v[:-1] + v[1:]) / 2
+    base = np.concatenate([mids, v, [448.0, 460.0, 464.0, 480.0, 1e4]])
+    xs = []
+    for m in base:
+        f = np.float32(m * s)
+        xs += [f, np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(-np.inf)),
+               np.nextafter(np.nextafter(f, np.float32(np.inf)), np.float32(np.inf))]
+    x = np.array(xs, np.float32)
+    x = np.concatenate([x, -x, np.float32([0.0, -0.0])])
+    x = np.concatenate([x, np.zeros((-len(x)) % 128, np.float32)])
+    xd = torch.from_numpy(x).to(DEV)
+    st = torch.tensor([s], dtype=torch.float32, device=DEV)
+    codes, sc = moe.moe_quantize_act(xd, static_scale=st)
+    torch.cuda.synchronize()
+    ref = oracle.quantize_e4m3(x, float(np.float32(s)))
+    got = codes.cpu().numpy()
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(x[i]), int(got[i]), int(ref[i])) for i in bad[:8]]
