@@ -7,10 +7,12 @@ T=8192 tokens, H=4096, I=1024, E=64, top-8 with Zipf(1.1)-skewed routing,
 the largest single-GPU configuration (the most tokens and flops);
 --workload / --tokens select the others.
 
-Prints one JSON line: tokens/s for the whole job (median step, each step
-after an L2/MALL flush), the roofline of the dominant kernel (the gate/up
-GEMM, HIP events around its launch inside the timed steps) and the fp64 CPU
-oracle timed on a bounded sample of the same batch on the host's cores.
+Prints one JSON line: tokens/s for the whole job (median of K replays of
+the step captured in a HIP graph, each replay after an L2/MALL flush; median,
+p10 and p90 in "timed", back-to-back replays in "warm"), the roofline of the
+dominant kernel (the gate/up GEMM, HIP events around its launch inside the
+timed steps) and the fp64 CPU oracle timed on a bounded sample of the same
+batch on the host's cores.
 """
 import argparse
 import hashlib
@@ -42,8 +44,8 @@ def kernel_source_sha():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill_bf16")
     ap.add_argument("--tokens", type=int, default=8192)
     ap.add_argument("--cpu-sample", type=int, default=64,
@@ -352,41 +354,82 @@ def main():
     K, W = args.steps, args.warmup
     st = torch.cuda.current_stream()
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def profiled_step(kev):
+        """route + align (+ the activation codes when x is quantised beside
+        the routing) -> forward, with HIP events around the GEMM launches."""
+        if args.persistent:  # the one launch of the forward between the kernel events
+            layer.prepare(x, logits)
+            ev.record(kev[0], st.cuda_stream)
+            layer.forward(x)
+            ev.record(kev[1], st.cuda_stream)
+        else:
+            layer(x, logits, events=kev)
+
+    layer(x, logits)  # first call outside any capture (loads the kernels)
+    torch.cuda.synchronize()
+    # One step (route -> align -> forward) captured in a HIP graph.
+    step_graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(st)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(step_graph, stream=cap):
+            layer(x, logits)
+    torch.cuda.synchronize()
     for _ in range(W):
+        step_graph.replay()
         layer(x, logits)
     torch.cuda.synchronize()
-    # Timed region: K steps, each after a 512 MiB write that evicts the L2s
-    # and the 256 MB MALL (so every step reads its weights from HBM), each
-    # bracketed by HIP events on the launch stream, with the library's events
-    # around the two GEMM launches inside the same steps.  The host queues the
-    # next flush and step while the GPU runs, so the steps are not host-paced.
-    sev = ev.create(2 * K)
+    # Timed region: K rounds of three steps, each step after a 512 MiB write
+    # that evicts the L2s and the 256 MB MALL (outside the step's events, so
+    # every step reads its weights from HBM), each bracketed by HIP events on
+    # the launch stream: a replay of the captured step (the headline), the
+    # same calls enqueued eagerly, and an eager step with the library's
+    # events around its GEMM launches (the kernel durations; events between
+    # kernels lengthen that step by a few us, so it is not the step time).
+    # The host queues the next flush and steps while the GPU runs, so no
+    # step is host-paced.
+    sev = ev.create(6 * K)
     kev = ev.create(4 * K)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
+        e6 = sev[6 * i: 6 * i + 6]
         flush.fill_(i & 0xFF)
-        ev.record(sev[2 * i], st.cuda_stream)
-        if args.persistent:  # the one launch of the forward between the kernel events
-            layer.prepare(x, logits)
-            ev.record(kev[4 * i], st.cuda_stream)
-            layer.forward(x)
-            ev.record(kev[4 * i + 1], st.cuda_stream)
-            ev.record(kev[4 * i + 2], st.cuda_stream)
-            ev.record(kev[4 * i + 3], st.cuda_stream)
-        else:
-            layer(x, logits, events=kev[4 * i: 4 * i + 4])
-        ev.record(sev[2 * i + 1], st.cuda_stream)
+        ev.record(e6[0], st.cuda_stream)
+        step_graph.replay()
+        ev.record(e6[1], st.cuda_stream)
+        flush.fill_((i + 85) & 0xFF)
+        ev.record(e6[2], st.cuda_stream)
+        layer(x, logits)
+        ev.record(e6[3], st.cuda_stream)
+        flush.fill_((i + 170) & 0xFF)
+        ev.record(e6[4], st.cuda_stream)
+        profiled_step(kev[4 * i: 4 * i + 4])
+        ev.record(e6[5], st.cuda_stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t0
-    step_us = np.array([ev.elapsed_ms(sev[2 * i], sev[2 * i + 1]) for i in range(K)]) * 1e3
-    g1_ms = sum(ev.elapsed_ms(kev[4 * i], kev[4 * i + 1]) for i in range(K)) / K
-    g2_ms = sum(ev.elapsed_ms(kev[4 * i + 2], kev[4 * i + 3]) for i in range(K)) / K
+    del step_graph
+
+    def span_us(evs, stride, a, b):
+        return np.array([ev.elapsed_ms(evs[stride * i + a], evs[stride * i + b])
+                         for i in range(K)]) * 1e3
+
+    def stats(us):
+        return {"median_us": round(float(np.median(us)), 2),
+                "p10_us": round(float(np.percentile(us, 10)), 2),
+                "p90_us": round(float(np.percentile(us, 90)), 2)}
+
+    step_us = span_us(sev, 6, 0, 1)
+    g1_ms = float(span_us(kev, 4, 0, 1).mean()) * 1e-3
+    g2_ms = 0.0 if args.persistent else float(span_us(kev, 4, 2, 3).mean()) * 1e-3
     med_us = float(np.median(step_us))
     ms_step = med_us * 1e-3
-    timed = {"median_us": round(med_us, 2), "p10_us": round(float(np.percentile(step_us, 10)), 2),
-             "p90_us": round(float(np.percentile(step_us, 90)), 2), "steps": K,
-             "flush_bytes": 512 << 20, "wall_s_incl_flushes": round(wall_s, 4)}
+    timed = dict(stats(step_us), steps=K, warmup=W, flush_bytes=512 << 20,
+                 protocol="replays of the step captured in one HIP graph",
+                 eager=stats(span_us(sev, 6, 2, 3)),
+                 profiled_step=stats(span_us(sev, 6, 4, 5)),
+                 wall_s_all_three_incl_flushes=round(wall_s, 4))
 
     # Warm, for context: K steps captured once into a HIP graph and replayed
     # back to back (as a serving loop runs them); between steps the MALL keeps
@@ -564,9 +607,10 @@ def main():
         "op_hbm_gbps": round(op_bytes / (ms_step * 1e-3) / 1e9, 1),
         "op_tflops": round(flops / (ms_step * 1e-3) / 1e12, 3),
         "down_gemm_avg_launch_us": None if args.persistent else round(g2_ms * 1e3, 2),
-        "timing": "median of K steps, each after a 512 MiB write that evicts L2 and the MALL, "
-                  "each timed with HIP events on the launch stream; GEMM durations from the "
-                  "library's events around its launches inside the same steps",
+        "timing": "median of K replays of the step captured in one HIP graph, each after a "
+                  "512 MiB write that evicts L2 and the MALL, timed with HIP events on the launch "
+                  "stream; GEMM durations from the library's events around its launches in K "
+                  "eager steps interleaved with the replays in the same timed region",
         "timed": timed,
         "roofline": roof,
         "cpu_baseline": cpu,

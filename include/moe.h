@@ -344,7 +344,10 @@ moe_status moe_fused_forward_persistent(
  * launch, and of events[2] / events[3] around the down GEMM launch (for
  * M <= 64 with f32 weights that launch also does the combine; otherwise the
  * combine kernel runs after events[3]).  NULL entries, or events == NULL,
- * are skipped.  For measuring kernel durations; no state is kept.
+ * are skipped.  Under stream capture each record is added to the graph as
+ * an event-record node, so every replay re-records the event at that point.
+ * A failed record returns MOE_ERR_HIP.  For measuring kernel durations; no
+ * state is kept.
  */
 moe_status moe_fused_forward_profiled(
     const moe_problem* p, const void* a, const void* w13, const void* w2,

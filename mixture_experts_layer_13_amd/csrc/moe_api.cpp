@@ -275,6 +275,32 @@ moe_status moe_route_align(const float* logits, int32_t M, int32_t E, int32_t to
 
 namespace {
 
+// Records a timing event on `st`.  Under stream capture the record is added
+// to the graph as an event-record node after the stream's current capture
+// dependencies (and becomes the new one), so every replay re-records the
+// event at that point; otherwise it is an ordinary hipEventRecord.
+int record_timing_event(void* ev, hipStream_t st) {
+  if (!ev) return 0;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  unsigned long long id = 0;
+  hipGraph_t graph = nullptr;
+  const hipGraphNode_t* deps = nullptr;
+  size_t ndeps = 0;
+  hipError_t e = hipStreamGetCaptureInfo_v2(st, &cs, &id, &graph, &deps, &ndeps);
+  if (e == hipSuccess) {
+    if (cs != hipStreamCaptureStatusActive) {
+      e = hipEventRecord((hipEvent_t)ev, st);
+    } else {
+      hipGraphNode_t node = nullptr;
+      e = hipGraphAddEventRecordNode(&node, graph, deps, ndeps, (hipEvent_t)ev);
+      if (e == hipSuccess)
+        e = hipStreamUpdateCaptureDependencies(st, &node, 1, hipStreamSetCaptureDependencies);
+    }
+  }
+  if (e != hipSuccess) (void)hipGetLastError();  // reported here, not by the next launch
+  return (int)e;
+}
+
 // moe_fused_forward with optional events around the two GEMM launches.
 moe_status fused_forward(const moe_problem* p, const void* a, const void* w13, const void* w2,
                          const float* w13_scale, const float* w2_scale, const float* a1_scale,
@@ -399,10 +425,10 @@ moe_status fused_forward(const moe_problem* p, const void* a, const void* w13, c
 
   void* prof[4];
   for (int i = 0; i < 4; ++i) prof[i] = events ? events[i] : nullptr;
-  if (prof[0]) (void)hipEventRecord((hipEvent_t)prof[0], st);
+  if ((err = record_timing_event(prof[0], st))) return hip_status(err, "timing event record");
   err = stream_path ? moe::launch_gemm1_stream(g, st) : moe::launch_gemm1_tile(g, st);
   if (err) return hip_status(err, "gate/up GEMM launch");
-  if (prof[1]) (void)hipEventRecord((hipEvent_t)prof[1], st);
+  if ((err = record_timing_event(prof[1], st))) return hip_status(err, "timing event record");
 
   if (fp8) {
     err = moe::launch_quant_h((const float*)g.h, p->N, (int)cap, num_padded, sorted_pair_ids, g.P,
@@ -414,19 +440,19 @@ moe_status fused_forward(const moe_problem* p, const void* a, const void* w13, c
     g.hq = g.h;
   }
 
-  if (prof[2]) (void)hipEventRecord((hipEvent_t)prof[2], st);
+  if ((err = record_timing_event(prof[2], st))) return hip_status(err, "timing event record");
   if (stream_path && !moe::gemm2_ring_applies(g)) {
     err = moe::launch_gemm2_stream(g, st);  // f32 weights: combine fused
     if (err) return hip_status(err, "down GEMM launch");
   } else {
     err = stream_path ? moe::launch_gemm2_ring(g, st) : moe::launch_gemm2_tile(g, st);
     if (err) return hip_status(err, "down GEMM launch");
-    if (prof[3]) (void)hipEventRecord((hipEvent_t)prof[3], st);
+    if ((err = record_timing_event(prof[3], st))) return hip_status(err, "timing event record");
     prof[3] = nullptr;
     err = moe::launch_combine(g, st);
     if (err) return hip_status(err, "combine launch");
   }
-  if (prof[3]) (void)hipEventRecord((hipEvent_t)prof[3], st);
+  if ((err = record_timing_event(prof[3], st))) return hip_status(err, "timing event record");
   return ok();
 }
 

@@ -511,6 +511,79 @@ def test_prequantised_step_in_a_graph():
     del g
 
 
+class _Events:
+    """Raw hipEvent_t handles, created and read through the HIP runtime."""
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.h = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            self.h.append(e.value)
+
+    def record(self, i, stream):
+        assert self.hip.hipEventRecord(self.ct.c_void_p(self.h[i]),
+                                       self.ct.c_void_p(stream.cuda_stream)) == 0
+
+    def ms(self, a, b):
+        v = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(v), self.ct.c_void_p(self.h[a]),
+                                          self.ct.c_void_p(self.h[b]))
+        assert rc == 0, rc
+        return v.value
+
+    def close(self):
+        for e in self.h:
+            self.hip.hipEventDestroy(self.ct.c_void_p(e))
+
+
+@pytest.mark.parametrize("wl,T", [("decode_fp8", 16), ("prefill_bf16", 1100)])
+def test_profiled_step_in_a_graph_records_its_events(wl, T):
+    """The step with the library's kernel events (moe_fused_forward_profiled)
+    captured in a graph: the events become event-record nodes that every
+    replay re-records, so the GEMM durations read after each replay are
+    positive and together fit inside the replay's own bracket, and the
+    output equals the eager step's."""
+    w = W[wl]
+    kw = {} if wl == "decode_fp8" else dict(H=512, I=256, E=16, topk=4)
+    d = inputs.make_inputs(w, T, device=DEV, seed=45, **kw)
+    H_, I_, E_, k_ = d["H"], d["I"], d["E"], d["topk"]
+    layer = moe.FusedMoE(T, H_, I_, E_, k_, d["w13"], d["w2"], d["w13_scale"], d["w2_scale"],
+                         a_dtype=d["x"].dtype, out_dtype=w.out_dtype, device=DEV)
+    ev = _Events(6)
+    eager = layer(d["x"], d["logits"], events=ev.h[:4]).clone()
+    torch.cuda.synchronize()
+    assert ev.ms(0, 1) > 0 and ev.ms(2, 3) > 0  # eager records
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            layer(d["x"], d["logits"], stream=s, events=ev.h[:4])
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    for r in range(3):
+        layer.out.zero_()
+        torch.cuda.synchronize()
+        ev.record(4, st)
+        g.replay()
+        ev.record(5, st)
+        torch.cuda.synchronize()
+        assert torch.equal(layer.out, eager), r
+        g1, g2, whole = ev.ms(0, 1), ev.ms(2, 3), ev.ms(4, 5)
+        assert g1 > 0 and g2 > 0 and g1 + g2 <= whole, (r, g1, g2, whole)
+        assert ev.ms(4, 0) >= 0 and ev.ms(3, 5) >= 0, r  # inside this replay's bracket
+    del g
+    ev.close()
+
+
 def _e4m3_positive_values():
     """The 127 non-negative finite E4M3FN values, ascending."""
     return np.array(sorted({float(oracle.e4m3_to_f64(c)) for c in range(0x7F)}), np.float64)
