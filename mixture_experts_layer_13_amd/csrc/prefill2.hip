@@ -39,6 +39,7 @@
 namespace moe {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kQRows = 256;                          // weight rows per tile
 constexpr int kQTok = 256;                           // token rows per tile
@@ -99,11 +100,21 @@ struct QTile {
   uint32_t xv[QL<NW>::Instr];
 };
 
+// The lane's index, recomputed at the point of use: a per-lane value kept
+// live across the whole tile loop for one use per tile is what the register
+// allocator spills first (and a reload from scratch memory waits for every
+// load and store in flight).
+__device__ __forceinline__ int q_lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // Metadata of token block mb into an LDS slot: 256 pair ids, then the
 // expert of the block (and 63 entries that are not used).
 template <int NW>
-__device__ __forceinline__ void q_meta_issue(const GemmArgs& a, char* slot, int mb, int valid, int wv,
-                                             int lane) {
+__device__ __forceinline__ void q_meta_issue(const GemmArgs& a, char* slot, int mb, int valid, int wv) {
+  const int lane = q_lane_here();
   if (wv < 4) {
     const auto ids = q_rsrc(a.sorted_ids + (size_t)mb * kQTok, valid ? kQTok * 4 : 0);
     q_dma4(ids, slot + wv * 256, ((uint32_t)lane + 64u * wv) * 4);
@@ -273,17 +284,20 @@ __device__ __forceinline__ void q_reads(QFrag<T, NW>& F, const char* stage, int 
 }
 
 // MFMA K of a half: bf16 K step K / (4 TA), block (K / 4 mod TA, K mod 4);
-// E4M3 block (K / 4, K mod 4).
-template <int T, int NW, int K>
+// E4M3 block (K / 4, K mod 4).  Z: the half is a tile's first, and its first
+// K step takes a zero accumulator operand (the MFMA's inline constant 0), so
+// that no register holds zeros for the next tile while the loop runs.
+template <int T, int NW, int K, bool Z>
 __device__ __forceinline__ void q_mma_one(f32x16 (&acc)[QL<NW>::TA][4], const QFrag<T, NW>& F) {
   constexpr int TA = QL<NW>::TA;
   if constexpr (T == DT_BF16) {
     constexpr int s = K / (4 * TA), i = (K / 4) % TA, j = K % 4;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(F.a[s][i]), as_bf16x8(F.b[s][j]), acc[i][j],
-                                                        0, 0, 0);
+    const f32x16 c = (Z && s == 0) ? f32x16{} : acc[i][j];
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(F.a[s][i]), as_bf16x8(F.b[s][j]), c, 0, 0, 0);
   } else {
     constexpr int i = K / 4, j = K % 4;
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[i], F.b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+    const f32x16 c = Z ? f32x16{} : acc[i][j];
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[i], F.b[j], c, 0, 0, 0, 0, 0, 0);
   }
 }
 
@@ -292,7 +306,7 @@ __device__ __forceinline__ void q_mma_one(f32x16 (&acc)[QL<NW>::TA][4], const QF
 // the MFMAs and (DMA) the ring loads evenly over all of them: the loads of
 // a CU's waves then arrive at about the rate its vector memory unit takes
 // them (bunched up, they stall the issuing wave and with it its MFMAs).
-template <int T, int NW, bool DMA, bool READ, int K = 0>
+template <int T, int NW, bool DMA, bool READ, bool Z = false, int K = 0>
 __device__ __forceinline__ void q_half(f32x16 (&acc)[QL<NW>::TA][4], const QFrag<T, NW>& Fc, QFrag<T, NW>& Fn,
                                        const char* rstage, int aoff, int boff, const int (&koff)[2],
                                        const QDma<NW>& d, const uint32_t (&wvoff)[2], int wv) {
@@ -300,7 +314,7 @@ __device__ __forceinline__ void q_half(f32x16 (&acc)[QL<NW>::TA][4], const QFrag
   constexpr int NM = (T == DT_BF16 ? 2 : 1) * L::TA * 4;
   constexpr int NI = 2 * L::Instr;
   if constexpr (K < NM) {
-    q_mma_one<T, NW, K>(acc, Fc);
+    q_mma_one<T, NW, K, Z>(acc, Fc);
     constexpr int span = NM * 3 / 4;
     constexpr int d0 = K < span ? K * L::ND / span : L::ND, d1 = K < span ? (K + 1) * L::ND / span : L::ND;
     if constexpr (READ) q_reads<T, NW, d0, d1>(Fn, rstage, aoff, boff, koff);
@@ -309,7 +323,7 @@ __device__ __forceinline__ void q_half(f32x16 (&acc)[QL<NW>::TA][4], const QFrag
       q_dmas<NW, v0, v1>(d, wvoff, wv);
     }
     __builtin_amdgcn_sched_barrier(0);
-    q_half<T, NW, DMA, READ, K + 1>(acc, Fc, Fn, rstage, aoff, boff, koff, d, wvoff, wv);
+    q_half<T, NW, DMA, READ, Z, K + 1>(acc, Fc, Fn, rstage, aoff, boff, koff, d, wvoff, wv);
   }
 }
 
@@ -319,7 +333,7 @@ __device__ __forceinline__ void q_half(f32x16 (&acc)[QL<NW>::TA][4], const QFrag
 // of tile src); multiply half 1 (F1) while reading half 0 of chunk c + 1
 // into F0 (LAST: not here; the last chunk of a tile leaves that read until
 // after the epilogue, so that the epilogue has the fragment registers).
-template <int T, bool G1, int NW, int ST, bool LAST = false>
+template <int T, bool G1, int NW, int ST, bool LAST = false, bool Z = false>
 __device__ __forceinline__ void q_step(const GemmArgs& a, f32x16 (&acc)[QL<NW>::TA][4], QFrag<T, NW>& F0,
                                        QFrag<T, NW>& F1, const QTile<NW>& src, int src_chunk, char* stage0,
                                        char* stage1, uint32_t rowb, const uint32_t (&wvoff)[2], int wv, int aoff,
@@ -327,7 +341,7 @@ __device__ __forceinline__ void q_step(const GemmArgs& a, f32x16 (&acc)[QL<NW>::
   char* cur = ST ? stage1 : stage0;
   char* next = ST ? stage0 : stage1;
   const QDma<NW> none{};
-  q_half<T, NW, false, true>(acc, F0, F1, cur, aoff, boff, koff[1], none, wvoff, wv);
+  q_half<T, NW, false, true, Z>(acc, F0, F1, cur, aoff, boff, koff[1], none, wvoff, wv);
   q_wait_vmcnt<0>();
   q_barrier();
   const QDma<NW> d = q_plan<G1, NW>(a, src, src_chunk, cur, rowb, wv);
@@ -427,36 +441,62 @@ __device__ __forceinline__ void q_epilogue(const GemmArgs& a, const f32x16 (&acc
 // row, so that every store instruction writes 8 whole 128-byte row segments
 // instead of 32 scattered 16-byte pieces (which the write path handles one
 // piece at a time).  Staging row t holds 16-byte column c at c ^ (t mod 8).
-// ES: output element bytes (2 bf16, 4 fp32); NB = 128 / (32 ES) 32-row
-// blocks per round.  val(ii, q, r) gives value r of rows 8 q + 4 h of block
-// ii of the round; out0 points at element (first token of the round, first
-// column of the round) of the output, row stride `stride` elements.
-template <int ES, typename V>
+// val(ii, q, r) gives value r of rows 8 q + 4 h of 32-row block ii of the
+// round (two blocks of bf16); out0 points at element (first token of the
+// round, first column of the round) of the output, row stride `stride`
+// elements.
+//
+// The staging accesses are written in assembly.  The compiler cannot tell
+// the staging area from the ring stages that the direct-to-LDS loads fill,
+// and before any LDS access it cannot place among those loads it waits for
+// every load in flight -- here the next tile's first ring loads and, at the
+// next tile's start, this epilogue's stores.  The staging area is the
+// wave's own and no load targets it; LDS operations of one wave complete in
+// order, so the reads see the writes, and the reads wait for themselves in
+// the same statement.
+__device__ __forceinline__ uint32_t q_lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+template <typename V>
 __device__ __forceinline__ void q_stage_round(char* stg, const int* ids, int tok0, int P, char* out0,
                                               size_t stride, int lane, V val) {
-  constexpr int NB = 128 / (32 * ES);
   const int r32 = lane & 31, hh = lane >> 5;
+  const uint32_t sbase = q_lds_addr(stg);
 #pragma unroll
-  for (int ii = 0; ii < NB; ++ii)
+  for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = val(ii, q, r);
-      const int b = (32 * ii + 8 * q + 4 * hh) * ES;
-      char* dst = stg + r32 * 128 + ((((b >> 4) ^ (r32 & 7))) << 4) + (b & 15);
-      if constexpr (ES == 2)
-        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      else
-        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+      const int b = (32 * ii + 8 * q + 4 * hh) * 2;
+      const uint32_t dst = sbase + r32 * 128 + ((((b >> 4) ^ (r32 & 7))) << 4) + (b & 15);
+      const u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      asm volatile("ds_write_b64 %0, %1" ::"v"(dst), "v"(pk) : "memory");
     }
   const int c = lane & 7;
+  uint32_t src[4];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const int t = (lane >> 3) + 8 * rr;
-    const i32x4 d = ld16(stg + t * 128 + ((c ^ (t & 7)) << 4));
+    src[rr] = sbase + t * 128 + ((c ^ (t & 7)) << 4);
+  }
+  i32x4 d[4];
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3])
+      : "v"(src[0]), "v"(src[1]), "v"(src[2]), "v"(src[3])
+      : "memory");
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int t = (lane >> 3) + 8 * rr;
     const int f = ids[tok0 + t];
-    if (f >= 0 && f < P) st16(out0 + ((size_t)t * stride) * ES + c * 16, d);
+    if (f >= 0 && f < P) st16(out0 + ((size_t)t * stride) * 2 + c * 16, d[rr]);
   }
   // one round at a time: keeps the scheduler from hoisting the accumulator
   // reads of later rounds (which would need more registers than there are)
@@ -482,22 +522,8 @@ __device__ __forceinline__ void q_epilogue_staged(const GemmArgs& a, const f32x1
     for (int ib = 0; ib < L::TA; ib += 2) {
       const int col = t.nt * kQRows + L::WaveRows * wr + 32 * ib;
       char* out0 = reinterpret_cast<char*>(a.y) + ((row0 + 32 * j) * a.K + col) * 2;
-      q_stage_round<2>(stg, ids, 128 * wc + 32 * j, a.P, out0, (size_t)a.K, lane,
+      q_stage_round(stg, ids, 128 * wc + 32 * j, a.P, out0, (size_t)a.K, lane,
                        [&](int ii, int q, int r) { return acc[ib + ii][j][4 * q + r] * scale; });
-    }
-}
-
-template <int TA>
-__device__ __forceinline__ void q_zero(f32x16 (&acc)[TA][4]) {
-  // the empty asm gives every zero accumulator an opaque value of its own,
-  // so that the compiler neither shares one zero register among them nor
-  // moves accumulators between registers inside the loop
-#pragma unroll
-  for (int i = 0; i < TA; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[i][j] = f32x16{};
-      asm volatile("" : "+a"(acc[i][j]));
     }
 }
 
@@ -555,7 +581,7 @@ __global__ __launch_bounds__(NW * 64) void pfq_gemm_kernel(GemmArgs a, int ntile
   cur.valid = 1;
   cur.mb = task / ntiles;
   cur.nt = task % ntiles;
-  q_meta_issue<NW>(a, meta, cur.mb, 1, wv, lane);
+  q_meta_issue<NW>(a, meta, cur.mb, 1, wv);
   q_scales_issue<T, G1, NW>(a, reinterpret_cast<char*>(scales), wv, lane);
   q_wait_vmcnt<0>();
   q_barrier();
@@ -568,11 +594,11 @@ __global__ __launch_bounds__(NW * 64) void pfq_gemm_kernel(GemmArgs a, int ntile
     const int tk = tn < end ? tn : task;
     nxt.mb = tk / ntiles;
     nxt.nt = tk % ntiles;
-    q_meta_issue<NW>(a, meta + kQMetaBytes, nxt.mb, nxt.valid, wv, lane);
+    q_meta_issue<NW>(a, meta + kQMetaBytes, nxt.mb, nxt.valid, wv);
   }
 
+  // every tile's first K step writes its accumulators from a zero operand
   f32x16 acc[L::TA][4];
-  q_zero<L::TA>(acc);
   QFrag<T, NW> F0, F1;
 
   // prologue: chunks 0 and 1 of the first tile, half 0 of chunk 0
@@ -592,8 +618,10 @@ __global__ __launch_bounds__(NW * 64) void pfq_gemm_kernel(GemmArgs a, int ntile
 
   while (true) {
     // step c refills stage c mod 2 with chunk c + 2 (of the next tile past
-    // the end of this one); the chunk count is even
-    for (int c = 0; c < nchunks - 2; c += 2) {
+    // the end of this one); the chunk count is even and at least 4
+    q_step<T, G1, NW, 0, false, true>(a, acc, F0, F1, cur, 2, stage0, stage1, rowb, wvoff, wv, aoff, boff, koff);
+    q_step<T, G1, NW, 1>(a, acc, F0, F1, cur, 3, stage0, stage1, rowb, wvoff, wv, aoff, boff, koff);
+    for (int c = 2; c < nchunks - 2; c += 2) {
       q_step<T, G1, NW, 0>(a, acc, F0, F1, cur, c + 2, stage0, stage1, rowb, wvoff, wv, aoff, boff, koff);
       q_step<T, G1, NW, 1>(a, acc, F0, F1, cur, c + 3, stage0, stage1, rowb, wvoff, wv, aoff, boff, koff);
     }
@@ -622,9 +650,8 @@ __global__ __launch_bounds__(NW * 64) void pfq_gemm_kernel(GemmArgs a, int ntile
       const int tk = tn < end ? tn : task;
       nxt.mb = tk / ntiles;
       nxt.nt = tk % ntiles;
-      q_meta_issue<NW>(a, meta + (slot ^ 1) * kQMetaBytes, nxt.mb, nxt.valid, wv, lane);
+      q_meta_issue<NW>(a, meta + (slot ^ 1) * kQMetaBytes, nxt.mb, nxt.valid, wv);
     }
-    q_zero<L::TA>(acc);
     q_reads<T, NW, 0, L::ND>(F0, stage0, aoff, boff, koff[0]);  // half 0 of the tile's chunk 0
   }
   q_wait_vmcnt<0>();  // no load may land after the workgroup's LDS is released
