@@ -353,7 +353,7 @@ __device__ __forceinline__ void q_step(const GemmArgs& a, f32x16 (&acc)[QL<NW>::
 // token column 32 j + lane % 32.  G1: scale, SiLU(gate) * up -> h (bf16, or
 // fp32 plus the running amax for E4M3); gate blocks i < TA / 2, up blocks
 // i + TA / 2.  G2: scale * (W2 h) -> y.
-template <int T, bool G1, int NW>
+template <int T, bool G1, int NW, bool PROBE>
 __device__ __forceinline__ void q_epilogue(const GemmArgs& a, const f32x16 (&acc)[QL<NW>::TA][4],
                                            const char* slot, const float* scales, const QTile<NW>& t, int wr,
                                            int wc, int lane) {
@@ -384,9 +384,9 @@ __device__ __forceinline__ void q_epilogue(const GemmArgs& a, const f32x16 (&acc
             }
             const int col = t.nt * 128 + (L::WaveRows / 2) * wr + 32 * i + 8 * q + 4 * hh;
             const size_t idx = (size_t)pos * a.N + col;
-            if (a.probe) {
+            if constexpr (PROBE) {
               probe_store(a, (size_t)pos, col, g4, u4);
-            } else if (T == DT_E4M3) {
+            } else if constexpr (T == DT_E4M3) {
               st16(reinterpret_cast<float*>(a.h) + idx,
                    i32x4{__float_as_int(h[0]), __float_as_int(h[1]), __float_as_int(h[2]), __float_as_int(h[3])});
 #pragma unroll
@@ -441,10 +441,10 @@ __device__ __forceinline__ void q_epilogue(const GemmArgs& a, const f32x16 (&acc
 // row, so that every store instruction writes 8 whole 128-byte row segments
 // instead of 32 scattered 16-byte pieces (which the write path handles one
 // piece at a time).  Staging row t holds 16-byte column c at c ^ (t mod 8).
-// val(ii, q, r) gives value r of rows 8 q + 4 h of 32-row block ii of the
-// round (two blocks of bf16); out0 points at element (first token of the
-// round, first column of the round) of the output, row stride `stride`
-// elements.
+// ES: output element bytes (2 bf16, 4 fp32); NB = 128 / (32 ES) 32-row
+// blocks per round.  val(ii, q, r) gives value r of rows 8 q + 4 h of block
+// ii of the round; out0 points at element (first token of the round, first
+// column of the round) of the output, row stride `stride` elements.
 //
 // The staging accesses are written in assembly.  The compiler cannot tell
 // the staging area from the ring stages that the direct-to-LDS loads fill,
@@ -458,22 +458,28 @@ __device__ __forceinline__ uint32_t q_lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-template <typename V>
+template <int ES, typename V>
 __device__ __forceinline__ void q_stage_round(char* stg, const int* ids, int tok0, int P, char* out0,
                                               size_t stride, int lane, V val) {
+  constexpr int NB = 128 / (32 * ES);
   const int r32 = lane & 31, hh = lane >> 5;
   const uint32_t sbase = q_lds_addr(stg);
 #pragma unroll
-  for (int ii = 0; ii < 2; ++ii)
+  for (int ii = 0; ii < NB; ++ii)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = val(ii, q, r);
-      const int b = (32 * ii + 8 * q + 4 * hh) * 2;
+      const int b = (32 * ii + 8 * q + 4 * hh) * ES;
       const uint32_t dst = sbase + r32 * 128 + ((((b >> 4) ^ (r32 & 7))) << 4) + (b & 15);
-      const u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      asm volatile("ds_write_b64 %0, %1" ::"v"(dst), "v"(pk) : "memory");
+      if constexpr (ES == 2) {
+        const u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        asm volatile("ds_write_b64 %0, %1" ::"v"(dst), "v"(pk) : "memory");
+      } else {
+        const f32x4 pk = {v[0], v[1], v[2], v[3]};
+        asm volatile("ds_write_b128 %0, %1" ::"v"(dst), "v"(pk) : "memory");
+      }
     }
   const int c = lane & 7;
   uint32_t src[4];
@@ -496,7 +502,7 @@ __device__ __forceinline__ void q_stage_round(char* stg, const int* ids, int tok
   for (int rr = 0; rr < 4; ++rr) {
     const int t = (lane >> 3) + 8 * rr;
     const int f = ids[tok0 + t];
-    if (f >= 0 && f < P) st16(out0 + ((size_t)t * stride) * 2 + c * 16, d[rr]);
+    if (f >= 0 && f < P) st16(out0 + ((size_t)t * stride) * ES + c * 16, d[rr]);
   }
   // one round at a time: keeps the scheduler from hoisting the accumulator
   // reads of later rounds (which would need more registers than there are)
@@ -505,6 +511,30 @@ __device__ __forceinline__ void q_stage_round(char* stg, const int* ids, int tok
 
 // Down-product epilogue through LDS (four-wave layout): y (bf16) in rounds
 // of 32 token rows x 64 columns.
+// Gate/up epilogue through LDS (four-wave layout, bf16 h): SiLU(gate) * up of
+// the wave's 64 intermediate columns x 128 token rows, one round of two
+// 32-column blocks per 32 token rows (gate blocks i < TA / 2, up blocks
+// i + TA / 2).  The stores from registers would write 8-byte pieces of 32
+// rows per instruction; the fp32 h of the E4M3 path already goes out as
+// 32-byte row pieces and is stored from registers.
+template <int NW>
+__device__ __forceinline__ void q_epilogue_g1_staged(const GemmArgs& a, const f32x16 (&acc)[QL<NW>::TA][4],
+                                                     const char* slot, const QTile<NW>& t, int wr, int wc,
+                                                     int lane, char* stg) {
+  using L = QL<NW>;
+  static_assert(L::TA == 4, "two gate and two up blocks per wave");
+  const int* ids = reinterpret_cast<const int*>(slot);
+  const size_t row0 = (size_t)t.mb * kQTok + 128 * wc;  // first token row of the wave
+  const int col0 = t.nt * 128 + (L::WaveRows / 2) * wr;  // first h column of the wave
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    char* out0 = reinterpret_cast<char*>(a.h) + ((row0 + 32 * j) * a.N + col0) * 2;
+    q_stage_round<2>(stg, ids, 128 * wc + 32 * j, a.P, out0, (size_t)a.N, lane, [&](int ii, int q, int r) {
+      return silu(acc[ii][j][4 * q + r]) * acc[ii + L::TA / 2][j][4 * q + r];
+    });
+  }
+}
+
 template <int T, int NW>
 __device__ __forceinline__ void q_epilogue_staged(const GemmArgs& a, const f32x16 (&acc)[QL<NW>::TA][4],
                                                   const char* slot, const float* scales, const QTile<NW>& t,
@@ -522,7 +552,7 @@ __device__ __forceinline__ void q_epilogue_staged(const GemmArgs& a, const f32x1
     for (int ib = 0; ib < L::TA; ib += 2) {
       const int col = t.nt * kQRows + L::WaveRows * wr + 32 * ib;
       char* out0 = reinterpret_cast<char*>(a.y) + ((row0 + 32 * j) * a.K + col) * 2;
-      q_stage_round(stg, ids, 128 * wc + 32 * j, a.P, out0, (size_t)a.K, lane,
+      q_stage_round<2>(stg, ids, 128 * wc + 32 * j, a.P, out0, (size_t)a.K, lane,
                        [&](int ii, int q, int r) { return acc[ib + ii][j][4 * q + r] * scale; });
     }
 }
@@ -534,7 +564,10 @@ __device__ __forceinline__ void q_epilogue_staged(const GemmArgs& a, const f32x1
 // contiguous ranges, one per XCD, and the workgroups of an XCD (the hardware
 // deals workgroup ids round-robin over the XCDs) take its tiles round-robin.
 // Needs an even number, at least 4, of chunks of 128 bytes of K.
-template <int T, bool G1, int NW>
+// PROBE: the test-only variant whose gate/up epilogue stores the scaled gate
+// and up sums (a.probe set); it keeps that epilogue out of the production
+// kernel, whose register budget has no room for two epilogues.
+template <int T, bool G1, int NW, bool PROBE>
 __global__ __launch_bounds__(NW * 64) void pfq_gemm_kernel(GemmArgs a, int ntiles) {
   using L = QL<NW>;
   // separate arrays, so that the compiler can tell the ring's two stages
@@ -544,7 +577,8 @@ __global__ __launch_bounds__(NW * 64) void pfq_gemm_kernel(GemmArgs a, int ntile
   __shared__ __attribute__((aligned(16))) char stage1[kQStage];
   __shared__ __attribute__((aligned(16))) char meta[2 * kQMetaBytes];
   __shared__ __attribute__((aligned(16))) float scales[1024 + 64];
-  __shared__ __attribute__((aligned(16))) char ystage[NW == 4 && !G1 ? 4 : 1][4096];  // staged down epilogue
+  // staged epilogues: the down product's, and the bf16 gate/up product's
+  __shared__ __attribute__((aligned(16))) char ystage[NW == 4 && (!G1 || (T == DT_BF16 && !PROBE)) ? 4 : 1][4096];
   const int lane = threadIdx.x & 63;
   const int wv = q_uniform(threadIdx.x >> 6);
   const int wr = wv / 2, wc = wv % 2;
@@ -631,12 +665,16 @@ __global__ __launch_bounds__(NW * 64) void pfq_gemm_kernel(GemmArgs a, int ntile
     q_tile_xv<G1, NW>(a, nxt, meta + (slot ^ 1) * kQMetaBytes, rowb, wv, lane);
     q_step<T, G1, NW, 0>(a, acc, F0, F1, nxt, 0, stage0, stage1, rowb, wvoff, wv, aoff, boff, koff);
     q_step<T, G1, NW, 1, true>(a, acc, F0, F1, nxt, 1, stage0, stage1, rowb, wvoff, wv, aoff, boff, koff);
-    // the gate/up epilogue stores straight from registers (staging it
-    // through LDS needs more registers than the wave has left)
-    if constexpr (NW == 4 && !G1)
+    // the epilogues stage through LDS (whole 128-byte row segments per
+    // store), except the E4M3 gate/up product's fp32 h and the test-only
+    // probe output, which store from registers
+    if constexpr (NW == 4 && !G1) {
       q_epilogue_staged<T, NW>(a, acc, meta + slot * kQMetaBytes, scales, cur, wr, wc, lane, ystage[wv]);
-    else
-      q_epilogue<T, G1, NW>(a, acc, meta + slot * kQMetaBytes, scales, cur, wr, wc, lane);
+    } else if constexpr (NW == 4 && T == DT_BF16 && !PROBE) {
+      q_epilogue_g1_staged<NW>(a, acc, meta + slot * kQMetaBytes, cur, wr, wc, lane, ystage[wv]);
+    } else {
+      q_epilogue<T, G1, NW, PROBE>(a, acc, meta + slot * kQMetaBytes, scales, cur, wr, wc, lane);
+    }
     task += stride;
     if (task >= end) break;
     cur = nxt;
@@ -689,7 +727,10 @@ static int pfq_launch(const GemmArgs& a, hipStream_t st) {
   long long g = tasks < device_cu_count() ? tasks : device_cu_count();
   g = g / 8 * 8;
   if (g < 8) g = 8;
-  hipLaunchKernelGGL((pfq_gemm_kernel<T, G1, NW>), dim3((unsigned)g), dim3(NW * 64), 0, st, a, ntiles);
+  if (G1 && a.probe)
+    hipLaunchKernelGGL((pfq_gemm_kernel<T, G1, NW, true>), dim3((unsigned)g), dim3(NW * 64), 0, st, a, ntiles);
+  else
+    hipLaunchKernelGGL((pfq_gemm_kernel<T, G1, NW, false>), dim3((unsigned)g), dim3(NW * 64), 0, st, a, ntiles);
   return (int)hipGetLastError();
 }
 
