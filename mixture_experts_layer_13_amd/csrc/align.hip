@@ -11,8 +11,10 @@
 // depends on the order in which atomics land.
 //
 //   chunk c = pairs [c*1024, (c+1)*1024), one 1024-thread workgroup each.
-//   hist kernel (only when there is more than one chunk): counts per chunk.
-//   scatter kernel: totals and the chunk's base per expert from the counts,
+//   hist kernel (only when there is more than one chunk): counts per chunk,
+//     stored expert-major.
+//   scatter kernel: totals and the chunk's base per expert from the counts
+//     (one wave per expert, its lanes across the chunks),
 //     padded offsets by a block scan, the in-chunk rank of each pair among
 //     equal ids (11-bit ballot match inside a wave + per-wave counts in LDS),
 //     then the writes; padding sentinels and block->expert entries are
@@ -35,8 +37,10 @@ __global__ __launch_bounds__(kChunk) void align_hist_kernel(
     if (id >= 0 && id < E) atomicAdd(&cnt[id], 1);
   }
   __syncthreads();
+  // expert-major [E][nchunks]: a scatter workgroup reads one expert's counts
+  // of all chunks as one contiguous run
   for (int e = threadIdx.x; e < E; e += kChunk)
-    hist[(size_t)blockIdx.x * E + e] = cnt[e];
+    hist[(size_t)e * gridDim.x + blockIdx.x] = cnt[e];
 }
 
 __global__ __launch_bounds__(kChunk) void align_scatter_kernel(

@@ -66,6 +66,19 @@ __device__ __forceinline__ void route_values(const float (&vin)[NPER], int E, in
       }
       need -= c;
     }
+    // every candidate left ranks above every key outside sel and cur: when
+    // exactly `need` are left they are the rest of the k
+    int left = 0;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) left += __popcll(cur[i]);
+    if (left == need) {
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) {
+        sel[i] |= cur[i];
+        cur[i] = 0;
+      }
+      need = 0;
+    }
   }
   // `cur` now holds equal keys: the lowest ids (i first, then lane) complete k
 #pragma unroll
@@ -177,7 +190,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
 
 // Alignment of chunk c (pairs [c*1024, c*1024+1024)) by a 1024-thread
 // workgroup.  With nchunks == 1 the chunk counts itself; otherwise hist
-// [nchunks][E] holds every chunk's counts.  Deterministic: LDS atomics only
+// [E][nchunks] holds every chunk's counts.  Deterministic: LDS atomics only
 // count, positions come from prefix sums and ballot ranks.
 // sm: LDS of (3E + 2 + 16(E+1) + 16) ints.
 __device__ __forceinline__ void align_chunk(
@@ -206,15 +219,20 @@ __device__ __forceinline__ void align_chunk(
       if (id >= 0 && id < E) atomicAdd(&total[id], 1);
     }
   } else {
-    for (int e = tid; e < E; e += kChunk) {
+    // one wave per expert, its lanes over the chunks (hist is [E][nchunks])
+    for (int e = w; e < E; e += kChunkWaves) {
       int t = 0, b = 0;
-      for (int cc = 0; cc < nchunks; ++cc) {
-        int h = hist[(size_t)cc * E + e];
+      for (int cc = lane; cc < nchunks; cc += kWave) {
+        const int h = hist[(size_t)e * nchunks + cc];
         if (cc < c) b += h;
         t += h;
       }
-      total[e] = t;
-      base[e] = b;
+      t = wave_sum_i(t);
+      b = wave_sum_i(b);
+      if (lane == 0) {
+        total[e] = t;
+        base[e] = b;
+      }
     }
   }
   for (int i = tid; i < kChunkWaves * (E + 1); i += kChunk) wcnt[i] = 0;
