@@ -28,16 +28,20 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 2500.0, "e4m3": 5000.0}
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 MFMA_FILE = os.path.join(ROOT, "profiles", "pmc_mfma.json")
-KERNEL_SRCS = [os.path.join(ROOT, "mixture_experts_layer_13_amd", "csrc", f)
-               for f in ("gemm.hip", "ring.hip", "ring.hpp", "prefill.hip", "prefill2.hip", "common.hpp")]
+# Sources of the gate/up kernel each stored counter record was taken with,
+# per kernel family (counters go stale when these change).
+_CSRC = os.path.join(ROOT, "mixture_experts_layer_13_amd", "csrc")
+KERNEL_SRCS = {
+    "decode": ["ring.hip", "ring.hpp", "fused.hip", "gemm.hip", "common.hpp", "launch.hpp"],
+    "prefill": ["prefill.hip", "prefill2.hip", "gemm.hip", "common.hpp", "launch.hpp"],
+}
 
 
-def kernel_source_sha():
-    """SHA-256 over the sources of the GEMM kernels (counters go stale when
-    these change)."""
+def kernel_source_sha(family):
+    """SHA-256 over the sources of one GEMM kernel family."""
     h = hashlib.sha256()
-    for f in KERNEL_SRCS:
-        h.update(open(f, "rb").read())
+    for f in KERNEL_SRCS[family]:
+        h.update(open(os.path.join(_CSRC, f), "rb").read())
     return h.hexdigest()
 
 
@@ -519,7 +523,7 @@ def main():
         roof["kernel"] = "gemm1_tile_kernel"
     roof["avg_launch_us"] = round(g1_ms * 1e3, 2)
     roof["algorithmic_bytes_per_launch"] = int(g1_bytes)
-    src_sha = kernel_source_sha()
+    src_sha = kernel_source_sha("decode" if (stream_path or args.persistent) else "prefill")
     key = f"{args.workload}:T{T}" + (":persistent" if args.persistent else "")
     if fp8:
         roof["x_quantised"] = ("beside the routing (moe_quantize_act)" if layer.prequant
