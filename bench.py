@@ -45,6 +45,49 @@ def kernel_source_sha(family):
     return h.hexdigest()
 
 
+def dense_gemm_context(layer, wl, H, I, dev, reps=20):
+    """The vendor library's dense GEMM (hipBLASLt through torch.mm, E4M3
+    through torch._scaled_mm) on the shapes the expert GEMMs execute: all
+    padded rows of this batch against one weight matrix of the gate/up
+    [2I, H] and down [H, I] products, each timed after the same 512 MiB flush
+    (median of `reps`).  A calibration of what a tuned dense GEMM reaches on
+    this chip at its clock under load, not a result of the layer."""
+    import torch
+
+    rows = int(layer.alignment.num_padded.item())
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    out = {"library": "hipBLASLt (torch.mm; E4M3: torch._scaled_mm)", "rows": rows}
+    for name, (k_, n_) in (("gate_up", (H, 2 * I)), ("down", (I, H))):
+        a = torch.randn(rows, k_, device=dev, dtype=torch.bfloat16, generator=g)
+        b = torch.randn(n_, k_, device=dev, dtype=torch.bfloat16, generator=g)
+        if wl.w_dtype == "e4m3":
+            a8, b8 = a.to(torch.float8_e4m3fn), b.to(torch.float8_e4m3fn)
+            one = torch.ones((), device=dev)
+
+            def fn():
+                return torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+        else:
+            def fn():
+                return torch.mm(a, b.t())
+        for _ in range(3):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            flush.fill_(1)
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
+        out[name] = {"m_k_n": [rows, k_, n_], "tflops": round(2.0 * rows * k_ * n_ / (ms * 1e-3) / 1e12, 1)}
+        del a, b
+    del flush
+    return out
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -471,6 +514,8 @@ def main():
     copy_gbps = 5 * 2 * (1 << 30) / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
     del ca, cb
     context = {"d2d_copy_gbps": round(copy_gbps, 1), "clocks": read_clocks()}
+    if T > 64 and wl.w_dtype in ("bf16", "e4m3"):
+        context["dense_gemm"] = dense_gemm_context(layer, wl, H, I, dev)
 
     if args.copy_check:  # plain copy of known size, for counter calibration
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -512,6 +557,10 @@ def main():
         peak = MFMA_PEAK_TFLOPS[wl.w_dtype]
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+        # the flops the kernel executes, the padding rows of the alignment
+        # blocks included (what the dense GEMM in "context" is comparable with)
+        rows = int(layer.alignment.num_padded.item())
+        roof["executed_tflops"] = round(4.0 * rows * H * I / (g1_ms * 1e-3) / 1e12, 2)
     ring = stream_path and wl.w_dtype in ("bf16", "e4m3") and (H * bw) % 512 == 0
     if args.persistent:
         roof["kernel"] = "fused_decode_kernel"
