@@ -8,8 +8,9 @@ the largest single-GPU configuration (the most tokens and flops);
 --workload / --tokens select the others.
 
 Prints one JSON line: tokens/s for the whole job (median of K replays of
-the step captured in a HIP graph, each replay after an L2/MALL flush; median,
-p10 and p90 in "timed", back-to-back replays in "warm"), the roofline of the
+the step captured in a HIP graph, each replay after a 512 MiB read that
+evicts the L2s and the MALL; median, p10 and p90 in "timed", back-to-back
+replays in "warm"), the roofline of the
 dominant kernel (the gate/up GEMM, HIP events around its launch inside the
 timed steps) and the fp64 CPU oracle timed on a bounded sample of the same
 batch on the host's cores.
@@ -45,6 +46,29 @@ def kernel_source_sha(family):
     return h.hexdigest()
 
 
+class CacheFlush:
+    """Evicts the L2s and the 256 MB MALL before a timed step by reading a
+    512 MiB buffer (a max-reduction into one word).  A read leaves the caches
+    holding clean lines.  A write of the same size (write(), the control)
+    leaves them dirty, and the step timed after it also pays for writing
+    those lines back to HBM."""
+
+    BYTES = 512 << 20
+
+    def __init__(self, dev):
+        import torch
+
+        self.torch = torch
+        self.buf = torch.full((self.BYTES // 4,), 3, dtype=torch.int32, device=dev)
+        self.sink = torch.empty((), dtype=torch.int32, device=dev)
+
+    def __call__(self):
+        self.torch.amax(self.buf, dim=0, out=self.sink)
+
+    def write(self, v):
+        self.buf.fill_(v)
+
+
 def dense_gemm_context(layer, wl, H, I, dev, reps=20):
     """The vendor library's dense GEMM (hipBLASLt through torch.mm, E4M3
     through torch._scaled_mm) on the shapes the expert GEMMs execute: all
@@ -55,7 +79,7 @@ def dense_gemm_context(layer, wl, H, I, dev, reps=20):
     import torch
 
     rows = int(layer.alignment.num_padded.item())
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = CacheFlush(dev)
     g = torch.Generator(device=dev)
     g.manual_seed(7)
     out = {"library": "hipBLASLt (torch.mm; E4M3: torch._scaled_mm)", "rows": rows}
@@ -76,7 +100,7 @@ def dense_gemm_context(layer, wl, H, I, dev, reps=20):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         torch.cuda.synchronize()
         for e0, e1 in ev:
-            flush.fill_(1)
+            flush()
             e0.record()
             fn()
             e1.record()
@@ -295,11 +319,11 @@ def rope_main(args):
     torch.cuda.synchronize()
     ev = HipEvents()
     st = torch.cuda.current_stream()
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = CacheFlush(dev)
     sev = ev.create(2 * K)
     torch.cuda.synchronize()
     for i in range(K):
-        flush.fill_(i & 0xFF)
+        flush()
         ev.record(sev[2 * i], st.cuda_stream)
         call()
         ev.record(sev[2 * i + 1], st.cuda_stream)
@@ -400,7 +424,7 @@ def main():
     ev = HipEvents()
     K, W = args.steps, args.warmup
     st = torch.cuda.current_stream()
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = CacheFlush(dev)
 
     def profiled_step(kev):
         """route + align (+ the activation codes when x is quantised beside
@@ -427,33 +451,38 @@ def main():
         step_graph.replay()
         layer(x, logits)
     torch.cuda.synchronize()
-    # Timed region: K rounds of three steps, each step after a 512 MiB write
+    # Timed region: K rounds of four steps, each step after a 512 MiB read
     # that evicts the L2s and the 256 MB MALL (outside the step's events, so
     # every step reads its weights from HBM), each bracketed by HIP events on
     # the launch stream: a replay of the captured step (the headline), the
-    # same calls enqueued eagerly, and an eager step with the library's
-    # events around its GEMM launches (the kernel durations; events between
-    # kernels lengthen that step by a few us, so it is not the step time).
-    # The host queues the next flush and steps while the GPU runs, so no
-    # step is host-paced.
-    sev = ev.create(6 * K)
+    # same calls enqueued eagerly, an eager step with the library's events
+    # around its GEMM launches (the kernel durations; events between kernels
+    # lengthen that step by a few us, so it is not the step time), and, as a
+    # control, a replay after a 512 MiB write instead of the read (the step
+    # then also writes the flush's dirty lines back).  The host queues the
+    # next flush and steps while the GPU runs, so no step is host-paced.
+    sev = ev.create(8 * K)
     kev = ev.create(4 * K)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        e6 = sev[6 * i: 6 * i + 6]
-        flush.fill_(i & 0xFF)
-        ev.record(e6[0], st.cuda_stream)
+        e8 = sev[8 * i: 8 * i + 8]
+        flush()
+        ev.record(e8[0], st.cuda_stream)
         step_graph.replay()
-        ev.record(e6[1], st.cuda_stream)
-        flush.fill_((i + 85) & 0xFF)
-        ev.record(e6[2], st.cuda_stream)
+        ev.record(e8[1], st.cuda_stream)
+        flush()
+        ev.record(e8[2], st.cuda_stream)
         layer(x, logits)
-        ev.record(e6[3], st.cuda_stream)
-        flush.fill_((i + 170) & 0xFF)
-        ev.record(e6[4], st.cuda_stream)
+        ev.record(e8[3], st.cuda_stream)
+        flush()
+        ev.record(e8[4], st.cuda_stream)
         profiled_step(kev[4 * i: 4 * i + 4])
-        ev.record(e6[5], st.cuda_stream)
+        ev.record(e8[5], st.cuda_stream)
+        flush.write(i & 0xFF)
+        ev.record(e8[6], st.cuda_stream)
+        step_graph.replay()
+        ev.record(e8[7], st.cuda_stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t0
     del step_graph
@@ -467,16 +496,17 @@ def main():
                 "p10_us": round(float(np.percentile(us, 10)), 2),
                 "p90_us": round(float(np.percentile(us, 90)), 2)}
 
-    step_us = span_us(sev, 6, 0, 1)
+    step_us = span_us(sev, 8, 0, 1)
     g1_ms = float(span_us(kev, 4, 0, 1).mean()) * 1e-3
     g2_ms = 0.0 if args.persistent else float(span_us(kev, 4, 2, 3).mean()) * 1e-3
     med_us = float(np.median(step_us))
     ms_step = med_us * 1e-3
-    timed = dict(stats(step_us), steps=K, warmup=W, flush_bytes=512 << 20,
-                 protocol="replays of the step captured in one HIP graph",
-                 eager=stats(span_us(sev, 6, 2, 3)),
-                 profiled_step=stats(span_us(sev, 6, 4, 5)),
-                 wall_s_all_three_incl_flushes=round(wall_s, 4))
+    timed = dict(stats(step_us), steps=K, warmup=W, flush_bytes=CacheFlush.BYTES,
+                 protocol="replays of the step captured in one HIP graph, each after a 512 MiB read",
+                 eager=stats(span_us(sev, 8, 2, 3)),
+                 profiled_step=stats(span_us(sev, 8, 4, 5)),
+                 replay_after_write_flush=stats(span_us(sev, 8, 6, 7)),
+                 wall_s_all_four_incl_flushes=round(wall_s, 4))
 
     # Warm, for context: K steps captured once into a HIP graph and replayed
     # back to back (as a serving loop runs them); between steps the MALL keeps
@@ -661,7 +691,7 @@ def main():
         "op_tflops": round(flops / (ms_step * 1e-3) / 1e12, 3),
         "down_gemm_avg_launch_us": None if args.persistent else round(g2_ms * 1e3, 2),
         "timing": "median of K replays of the step captured in one HIP graph, each after a "
-                  "512 MiB write that evicts L2 and the MALL, timed with HIP events on the launch "
+                  "512 MiB read that evicts L2 and the MALL, timed with HIP events on the launch "
                   "stream; GEMM durations from the library's events around its launches in K "
                   "eager steps interleaved with the replays in the same timed region",
         "timed": timed,
