@@ -394,9 +394,8 @@ def rope_main(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the layer is single-GPU; see the design notes for how it would shard)",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer runs "
+              "on one GPU: no collectives, no sharding)", file=sys.stderr)
         sys.exit(2)
     if args.router:
         router_main(args)

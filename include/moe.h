@@ -60,7 +60,7 @@ typedef enum {
   MOE_ERR_DTYPE = 3,       /* an unknown dtype code */
   MOE_ERR_ALIGN = 4,       /* a pointer is not aligned as required */
   MOE_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
-  MOE_ERR_UNSUPPORTED = 6, /* valid values this build does not handle */
+  MOE_ERR_UNSUPPORTED = 6, /* valid values the library does not handle */
   MOE_ERR_HIP = 7          /* the HIP runtime rejected a launch */
 } moe_status;
 
