@@ -434,17 +434,17 @@ __device__ __forceinline__ void q_epilogue(const GemmArgs& a, const f32x16 (&acc
   }
 }
 
-// Epilogue through LDS (four-wave layout, no probe): the wave's result is
-// written to memory in rounds of 32 token rows x 128 bytes.  Each lane first
-// puts its MFMA results (4 consecutive rows of one token) into a 4 KiB
-// staging area of the wave, then reads back 16 contiguous bytes of a token
-// row, so that every store instruction writes 8 whole 128-byte row segments
-// instead of 32 scattered 16-byte pieces (which the write path handles one
-// piece at a time).  Staging row t holds 16-byte column c at c ^ (t mod 8).
-// ES: output element bytes (2 bf16, 4 fp32); NB = 128 / (32 ES) 32-row
-// blocks per round.  val(ii, q, r) gives value r of rows 8 q + 4 h of block
-// ii of the round; out0 points at element (first token of the round, first
-// column of the round) of the output, row stride `stride` elements.
+// Epilogue through LDS (four-wave layout, bf16 output): the wave's result is
+// written to memory in rounds of 32 token rows x 128 bytes (two 32-column
+// blocks).  Each lane first puts its MFMA results (4 consecutive rows of one
+// token) into a 4 KiB staging area of the wave, then reads back 16
+// contiguous bytes of a token row, so that every store instruction writes 8
+// whole 128-byte row segments instead of 32 scattered 8-byte pieces (which
+// the write path handles one piece at a time).  Staging row t holds 16-byte
+// column c at c ^ (t mod 8).  val(ii, q, r) gives value r of rows 8 q + 4 h
+// of block ii of the round; out0 points at element (first token of the
+// round, first column of the round) of the output, row stride `stride`
+// elements.
 //
 // The staging accesses are written in assembly.  The compiler cannot tell
 // the staging area from the ring stages that the direct-to-LDS loads fill,
@@ -458,28 +458,22 @@ __device__ __forceinline__ uint32_t q_lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-template <int ES, typename V>
+template <typename V>
 __device__ __forceinline__ void q_stage_round(char* stg, const int* ids, int tok0, int P, char* out0,
                                               size_t stride, int lane, V val) {
-  constexpr int NB = 128 / (32 * ES);
   const int r32 = lane & 31, hh = lane >> 5;
   const uint32_t sbase = q_lds_addr(stg);
 #pragma unroll
-  for (int ii = 0; ii < NB; ++ii)
+  for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = val(ii, q, r);
-      const int b = (32 * ii + 8 * q + 4 * hh) * ES;
+      const int b = (32 * ii + 8 * q + 4 * hh) * 2;
       const uint32_t dst = sbase + r32 * 128 + ((((b >> 4) ^ (r32 & 7))) << 4) + (b & 15);
-      if constexpr (ES == 2) {
-        const u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        asm volatile("ds_write_b64 %0, %1" ::"v"(dst), "v"(pk) : "memory");
-      } else {
-        const f32x4 pk = {v[0], v[1], v[2], v[3]};
-        asm volatile("ds_write_b128 %0, %1" ::"v"(dst), "v"(pk) : "memory");
-      }
+      const u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      asm volatile("ds_write_b64 %0, %1" ::"v"(dst), "v"(pk) : "memory");
     }
   const int c = lane & 7;
   uint32_t src[4];
@@ -502,15 +496,13 @@ __device__ __forceinline__ void q_stage_round(char* stg, const int* ids, int tok
   for (int rr = 0; rr < 4; ++rr) {
     const int t = (lane >> 3) + 8 * rr;
     const int f = ids[tok0 + t];
-    if (f >= 0 && f < P) st16(out0 + ((size_t)t * stride) * ES + c * 16, d[rr]);
+    if (f >= 0 && f < P) st16(out0 + ((size_t)t * stride) * 2 + c * 16, d[rr]);
   }
   // one round at a time: keeps the scheduler from hoisting the accumulator
   // reads of later rounds (which would need more registers than there are)
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Down-product epilogue through LDS (four-wave layout): y (bf16) in rounds
-// of 32 token rows x 64 columns.
 // Gate/up epilogue through LDS (four-wave layout, bf16 h): SiLU(gate) * up of
 // the wave's 64 intermediate columns x 128 token rows, one round of two
 // 32-column blocks per 32 token rows (gate blocks i < TA / 2, up blocks
@@ -529,12 +521,14 @@ __device__ __forceinline__ void q_epilogue_g1_staged(const GemmArgs& a, const f3
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     char* out0 = reinterpret_cast<char*>(a.h) + ((row0 + 32 * j) * a.N + col0) * 2;
-    q_stage_round<2>(stg, ids, 128 * wc + 32 * j, a.P, out0, (size_t)a.N, lane, [&](int ii, int q, int r) {
+    q_stage_round(stg, ids, 128 * wc + 32 * j, a.P, out0, (size_t)a.N, lane, [&](int ii, int q, int r) {
       return silu(acc[ii][j][4 * q + r]) * acc[ii + L::TA / 2][j][4 * q + r];
     });
   }
 }
 
+// Down-product epilogue through LDS (four-wave layout): y (bf16) in rounds
+// of 32 token rows x 64 columns.
 template <int T, int NW>
 __device__ __forceinline__ void q_epilogue_staged(const GemmArgs& a, const f32x16 (&acc)[QL<NW>::TA][4],
                                                   const char* slot, const float* scales, const QTile<NW>& t,
@@ -552,7 +546,7 @@ __device__ __forceinline__ void q_epilogue_staged(const GemmArgs& a, const f32x1
     for (int ib = 0; ib < L::TA; ib += 2) {
       const int col = t.nt * kQRows + L::WaveRows * wr + 32 * ib;
       char* out0 = reinterpret_cast<char*>(a.y) + ((row0 + 32 * j) * a.K + col) * 2;
-      q_stage_round<2>(stg, ids, 128 * wc + 32 * j, a.P, out0, (size_t)a.K, lane,
+      q_stage_round(stg, ids, 128 * wc + 32 * j, a.P, out0, (size_t)a.K, lane,
                        [&](int ii, int q, int r) { return acc[ib + ii][j][4 * q + r] * scale; });
     }
 }
