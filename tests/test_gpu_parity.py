@@ -454,6 +454,35 @@ def test_forward_full_size_sampled_tokens(wl, T):
     assert (o.abs().amax(dim=1) > 0).all()
 
 
+# The same check on batches drawn from other seeds (new x, logits and
+# weights): the routing and the per-tensor scales change with them, and so do
+# the expert loads, padding and tile counts the kernels walk.
+SEEDED = [(wl, T, sd) for wl, T in [("decode_bf16", 64), ("decode_fp8", 64), ("large_fp8", 64),
+                                     ("large_fp8", 256), ("prefill_bf16", 8192), ("prefill_fp8", 8192)]
+          for sd in (11, 3333)]
+
+
+@pytest.mark.parametrize("wl,T,sd", SEEDED, ids=[f"{a}-T{b}-seed{c}" for a, b, c in SEEDED])
+def test_forward_full_size_other_seeds(wl, T, sd):
+    w = W[wl]
+    d = inputs.make_inputs(w, T, device=DEV, seed=90000 + 7 * sd + T)
+    layer, out = H.run_gpu(d)
+    rids, _ = oracle.route_topk(d["logits"].cpu().numpy(), d["topk"], True)
+    assert np.array_equal(layer.topk_ids.cpu().numpy(), rids)
+    tokens = H.sample_tokens(rids, 128, seed=sd)
+    label = f"{wl} T={T} seed {sd} block_m={layer.block_m}"
+    if w.fp8_act:
+        H.check_fp8_dynamic(d, layer.act_scales(), out, tokens, label)
+    else:
+        ref, _, _, _ = H.oracle_forward(d, tokens=tokens)
+        err = H.row_rel_err(H.to_f64(out)[tokens], ref)
+        H.say(f"  {label}: {len(tokens)} rows, max row rel err {err:.3e}")
+        assert err <= H.BF16_TOL, err
+    o = out.float()
+    assert torch.isfinite(o).all()
+    assert (o.abs().amax(dim=1) > 0).all()
+
+
 # ------------------------------------------- pre-quantised activations
 
 PREQUANT = [("decode_fp8", 1, {}), ("decode_fp8", 3, {}), ("decode_fp8", 8, {}),
