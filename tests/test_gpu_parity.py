@@ -279,6 +279,12 @@ SMALL = [
     ("fp8_T64", "decode_fp8", 64, 512, 384, 16, 8, 32),
     ("fp8_T100_tile", "decode_fp8", 100, 512, 256, 16, 4, 64),
     ("fp8_T257_tile", "large_fp8", 257, 768, 256, 32, 8, 128),
+    # degenerate routings: every expert for every token (k = E = 64, the
+    # largest k; more than one alignment chunk of pairs at 20 tokens), and
+    # top-1
+    ("bf16_T20_k64_E64", "decode_bf16", 20, 512, 256, 64, 64, 16),
+    ("fp8_T3_k64_E64", "decode_fp8", 3, 512, 256, 64, 64, 16),
+    ("bf16_T50_k1", "decode_bf16", 50, 512, 256, 16, 1, 16),
 ]
 
 # Large-batch kernels (alignment blocks of 128 or 256 rows): 1, 2, 3, 4 and 5
